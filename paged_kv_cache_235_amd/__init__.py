@@ -1,0 +1,20 @@
+"""Paged-KV attention for AMD Instinct MI355X (gfx950).
+
+Python binding of libpagedkv, whose C ABI is ``include/pagedkv.h``:
+
+* ``kv_cache_write``  -- store new K/V vectors in physical block slots
+  (bf16/fp32 copy, or INT8 with a dynamic per-vector fp16 scale);
+* ``paged_attention_decode`` -- one query token per sequence, split over
+  partitions of the context and merged (log-sum-exp);
+* ``paged_attention_prefill_chunk`` -- a chunk of query tokens per sequence
+  with causal and sliding-window masks, on bf16 MFMA.
+
+The library is loaded on first use; there is no CPU fallback.
+"""
+from ._binding import (EXPORTS, LIB_PATH, CacheDesc, PagedKVError, cache_desc, decode_workspace_size,
+                       kv_cache_write, last_error, load_library, paged_attention_decode,
+                       paged_attention_prefill_chunk, set_decode_split_event, version)
+
+__all__ = ["EXPORTS", "LIB_PATH", "CacheDesc", "PagedKVError", "cache_desc", "decode_workspace_size",
+           "kv_cache_write", "last_error", "load_library", "paged_attention_decode",
+           "paged_attention_prefill_chunk", "set_decode_split_event", "version"]

@@ -1,0 +1,250 @@
+"""ctypes binding of libpagedkv (include/pagedkv.h) for torch tensors.
+
+Argument marshalling only: tensors are checked (device, dtype, shape,
+contiguity) and passed as device pointers together with torch's current HIP
+stream; every step of the computation runs in the library's kernels.  There
+is no fallback: if ``libpagedkv.so`` is not built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libpagedkv.so")
+
+PKV_F32, PKV_BF16, PKV_I8 = 1, 2, 4
+_TORCH_TO_PKV = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16, torch.int8: PKV_I8}
+STATUS = {0: "PKV_OK", 1: "PKV_EINVAL", 2: "PKV_EUNSUPPORTED", 3: "PKV_EWORKSPACE", 4: "PKV_EHIP"}
+
+# every symbol include/pagedkv.h declares
+EXPORTS = ("kv_cache_write", "paged_attention_decode_workspace_size", "paged_attention_decode",
+           "paged_attention_prefill_chunk", "pkv_last_error", "pkv_version",
+           "pkv_profile_set_decode_split_event")
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("kv_dtype", ctypes.c_int32)]
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libpagedkv (once).  Raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(path):
+                raise ImportError(f"{path} is missing: build it with `python -m paged_kv_cache_235_amd._build` "
+                                  "(or __graft_entry__.build()); there is no fallback implementation")
+            lib = ctypes.CDLL(path)
+            P, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+            D = ctypes.POINTER(CacheDesc)
+            lib.kv_cache_write.restype = ctypes.c_int
+            lib.kv_cache_write.argtypes = [D, P, P, i32, i64, P, i32, P, P, P, P, P]
+            lib.paged_attention_decode_workspace_size.restype = ctypes.c_size_t
+            lib.paged_attention_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+            lib.paged_attention_decode.restype = ctypes.c_int
+            lib.paged_attention_decode.argtypes = [D, P, i32, P, i32, i32, i32, P, P, P, P, P, i32, P,
+                                                   f32, i32, i32, P, ctypes.c_size_t, P]
+            lib.paged_attention_prefill_chunk.restype = ctypes.c_int
+            lib.paged_attention_prefill_chunk.argtypes = [D, P, i32, P, i32, P, i32, i32, i32, P, P, P, i32,
+                                                          P, f32, i32, P]
+            lib.pkv_last_error.restype = ctypes.c_char_p
+            lib.pkv_last_error.argtypes = []
+            lib.pkv_version.restype = ctypes.c_char_p
+            lib.pkv_version.argtypes = []
+            lib.pkv_profile_set_decode_split_event.restype = ctypes.c_int
+            lib.pkv_profile_set_decode_split_event.argtypes = [P]
+            _lib = lib
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise PagedKVError(status, load_library().pkv_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype(t: torch.Tensor, what: str) -> int:
+    try:
+        return _TORCH_TO_PKV[t.dtype]
+    except KeyError:
+        raise TypeError(f"{what}: unsupported dtype {t.dtype}") from None
+
+
+def _on_gpu(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("tensors must be on the GPU")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("tensors must be on one GPU")
+    return dev
+
+
+def _contig(t, what):
+    if t is not None and not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+
+
+def cache_desc(k_pool: torch.Tensor) -> CacheDesc:
+    """Descriptor of a pool shaped [num_blocks][num_kv_heads][block_size][head_dim]."""
+    if k_pool.dim() != 4:
+        raise ValueError("pools are [num_blocks][num_kv_heads][block_size][head_dim]")
+    nb, hkv, bs, d = k_pool.shape
+    return CacheDesc(nb, bs, hkv, d, _dtype(k_pool, "pool"))
+
+
+def _check_pools(k_pool, v_pool, k_scale, v_scale):
+    if v_pool.shape != k_pool.shape or v_pool.dtype != k_pool.dtype:
+        raise ValueError("k_pool and v_pool differ in shape or dtype")
+    _contig(k_pool, "k_pool")
+    _contig(v_pool, "v_pool")
+    if k_pool.dtype == torch.int8:
+        if k_scale is None or v_scale is None:
+            raise ValueError("INT8 pools need k_scale and v_scale")
+        for sc in (k_scale, v_scale):
+            if sc.shape != k_pool.shape[:3] or sc.dtype not in (torch.float16, torch.int16):
+                raise ValueError("scale pools are fp16 [num_blocks][num_kv_heads][block_size]")
+            _contig(sc, "scale pool")
+
+
+def kv_cache_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
+                   k_pool: torch.Tensor, v_pool: torch.Tensor,
+                   k_scale: torch.Tensor | None = None, v_scale: torch.Tensor | None = None) -> None:
+    """Store k, v ([T][Hkv][D], token stride may exceed Hkv*D) into their slots."""
+    dev = _on_gpu(k, v, slot_mapping, k_pool, v_pool, k_scale, v_scale)
+    _check_pools(k_pool, v_pool, k_scale, v_scale)
+    desc = cache_desc(k_pool)
+    if k.dim() != 3 or k.shape != v.shape or k.stride() != v.stride() or k.dtype != v.dtype:
+        raise ValueError("k and v must both be [num_tokens][num_kv_heads][head_dim] with equal strides")
+    if k.stride(2) != 1 or k.stride(1) != k.shape[2]:
+        raise ValueError("each token's heads must be dense (stride only between tokens)")
+    if slot_mapping.dtype != torch.int32 or slot_mapping.dim() != 1 or slot_mapping.shape[0] != k.shape[0]:
+        raise ValueError("slot_mapping must be int32 [num_tokens]")
+    _contig(slot_mapping, "slot_mapping")
+    stride = k.stride(0) if k.shape[0] > 1 else k.shape[1] * k.shape[2]
+    lib = load_library()
+    _check(lib.kv_cache_write(ctypes.byref(desc), _ptr(k), _ptr(v), _dtype(k, "k"), stride,
+                              _ptr(slot_mapping), k.shape[0], _ptr(k_pool), _ptr(v_pool), _ptr(k_scale),
+                              _ptr(v_scale), _stream(dev)))
+
+
+def decode_workspace_size(num_seqs: int, num_q_heads: int, head_dim: int, max_blocks_per_seq: int,
+                          block_size: int = 16, partition_size: int = 512) -> int:
+    return int(load_library().paged_attention_decode_workspace_size(
+        num_seqs, num_q_heads, head_dim, max_blocks_per_seq, block_size, partition_size))
+
+
+def paged_attention_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                           block_tables: torch.Tensor, context_lens: torch.Tensor, softmax_scale: float,
+                           sliding_window: int = 0, partition_size: int = 512,
+                           k_scale: torch.Tensor | None = None, v_scale: torch.Tensor | None = None,
+                           out: torch.Tensor | None = None, out_dtype: torch.dtype = torch.float32,
+                           workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Decode attention for q [num_seqs][Hq][D]; returns out [num_seqs][Hq][D]."""
+    dev = _on_gpu(q, k_pool, v_pool, block_tables, context_lens, k_scale, v_scale, out, workspace)
+    _check_pools(k_pool, v_pool, k_scale, v_scale)
+    desc = cache_desc(k_pool)
+    _contig(q, "q")
+    if q.dim() != 3 or q.shape[2] != desc.head_dim:
+        raise ValueError("q must be [num_seqs][num_q_heads][head_dim]")
+    b, hq, d = q.shape
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != b:
+        raise ValueError("block_tables must be int32 [num_seqs][max_blocks_per_seq]")
+    if context_lens.dtype != torch.int32 or context_lens.shape != (b,):
+        raise ValueError("context_lens must be int32 [num_seqs]")
+    _contig(block_tables, "block_tables")
+    _contig(context_lens, "context_lens")
+    if out is None:
+        out = torch.empty((b, hq, d), dtype=out_dtype, device=q.device)
+    elif out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    _contig(out, "out")
+    maxb = max(block_tables.shape[1], 1)
+    need = decode_workspace_size(b, hq, d, maxb, desc.block_size, partition_size) if b else 0
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    lib = load_library()
+    _check(lib.paged_attention_decode(
+        ctypes.byref(desc), _ptr(q), _dtype(q, "q"), _ptr(out), _dtype(out, "out"), b, hq, _ptr(k_pool),
+        _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), maxb, _ptr(context_lens),
+        float(softmax_scale), int(sliding_window), int(partition_size), _ptr(workspace) if need else None,
+        need, _stream(dev)))
+    return out
+
+
+def paged_attention_prefill_chunk(q: torch.Tensor, cu_q_lens: torch.Tensor, seq_lens: torch.Tensor,
+                                  k_pool: torch.Tensor, v_pool: torch.Tensor, block_tables: torch.Tensor,
+                                  max_q_len: int, softmax_scale: float, sliding_window: int = 0,
+                                  out: torch.Tensor | None = None,
+                                  out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """Chunked-prefill attention for q [total_rows][Hq][D] (bf16)."""
+    dev = _on_gpu(q, cu_q_lens, seq_lens, k_pool, v_pool, block_tables, out)
+    _check_pools(k_pool, v_pool, None, None)
+    desc = cache_desc(k_pool)
+    _contig(q, "q")
+    if q.dim() != 3 or q.shape[2] != desc.head_dim:
+        raise ValueError("q must be [total_rows][num_q_heads][head_dim]")
+    b = seq_lens.shape[0]
+    if cu_q_lens.dtype != torch.int32 or cu_q_lens.shape != (b + 1,):
+        raise ValueError("cu_q_lens must be int32 [num_seqs + 1]")
+    if seq_lens.dtype != torch.int32 or seq_lens.dim() != 1:
+        raise ValueError("seq_lens must be int32 [num_seqs]")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != b:
+        raise ValueError("block_tables must be int32 [num_seqs][max_blocks_per_seq]")
+    for t, n in ((cu_q_lens, "cu_q_lens"), (seq_lens, "seq_lens"), (block_tables, "block_tables")):
+        _contig(t, n)
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    elif out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    _contig(out, "out")
+    lib = load_library()
+    _check(lib.paged_attention_prefill_chunk(
+        ctypes.byref(desc), _ptr(q), _dtype(q, "q"), _ptr(out), _dtype(out, "out"), _ptr(cu_q_lens), b,
+        int(max_q_len), q.shape[1], _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+        max(block_tables.shape[1], 1), _ptr(seq_lens), float(softmax_scale), int(sliding_window), _stream(dev)))
+    return out
+
+
+def set_decode_split_event(event) -> None:
+    """Profiling aid: record ``event`` (torch.cuda.Event or None) between the
+    decode partition and merge kernels of later decode calls on this thread."""
+    if event is not None and not event.cuda_event:
+        event.record()          # torch creates the HIP event on first record
+    ptr = None if event is None else ctypes.c_void_p(event.cuda_event)
+    load_library().pkv_profile_set_decode_split_event(ptr)
+
+
+def last_error() -> str:
+    return load_library().pkv_last_error().decode()
+
+
+def version() -> str:
+    return load_library().pkv_version().decode()

@@ -1,0 +1,604 @@
+// decode.hip -- paged attention for one query token per sequence.
+//
+// "PyTorch LLM Serving Engine", Loading and What is implemented: attend while
+// walking the sequence's block table with a numerically stable online
+// softmax.  "MicroGen", Key Features: grouped-query attention (every KV head
+// serves G query heads), dynamic INT8 KV, window-length limit.
+//
+// Work decomposition (gfx950, wave64):
+//  * A work item is (sequence, partition of the context, KV head, chunk of at
+//    most 8 of its query heads).  The kernel is persistent: each workgroup
+//    first turns the context lengths into a prefix of per-sequence partition
+//    counts in LDS, then strides over the items.  No host knowledge of the
+//    lengths is needed and no empty workgroup is launched.
+//  * Inside an item the keys are taken in chunks of up to 512 tokens aligned
+//    to 512.  Phase 1: each of the 4 waves streams whole (block, KV head)
+//    K tiles -- one contiguous run, read with coalesced 16-byte loads -- and
+//    forms all the query heads' dot products from the same registers (one K
+//    read serves the whole group).  The per-lane partial sums are reduced
+//    with a transposed DPP butterfly and the scaled logits land in LDS.
+//    Softmax: the workgroup takes the chunk's maximum and exponentiates each
+//    logit once (exp2, scale * log2 e folded in).  Phase 2: the waves stream
+//    the V tiles of the same blocks and accumulate p * v.  Chunks are merged
+//    with the running-maximum rescale, so every K/V byte is read once.
+//  * Keys outside the sequence, its window or a valid block are removed by
+//    selection (logit -inf, V row zeroed), never by multiplying by zero, so
+//    poisoned (NaN) tail slots cannot leak.
+//  * With more than one partition per sequence the items write unnormalised
+//    partial results (m, l, o) and a second kernel merges them (log-sum-exp).
+#include "pkv_internal.h"
+#include "pkv_device.h"
+
+namespace pkv {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kChunk = 512;            // keys per softmax chunk
+constexpr int kBlk = 16;               // tokens per cache block
+constexpr int kMaxSeqs = 2048;         // sequences per launch (LDS prefix)
+constexpr int kMaxGroup = 8;           // query heads per item
+
+struct DecodeArgs {
+    const void* q;
+    void* out;
+    float* part_ml;          // [num_seqs][Hq][max_parts][2]  running max (log2 units), sum
+    float* part_o;           // [num_seqs][Hq][max_parts][D]  unnormalised outputs
+    const char* k_pool;
+    const char* v_pool;
+    const uint16_t* k_scale;
+    const uint16_t* v_scale;
+    const int32_t* block_tables;
+    const int32_t* context_lens;
+    int32_t num_seqs, num_q_heads, num_kv_heads, group, head_chunks, num_blocks, max_blocks;
+    int32_t window, part_tokens, max_parts;
+    float scale_log2;        // softmax_scale * log2(e)
+    int32_t q_bf16, out_bf16;
+};
+
+template <int KV> struct KvT;
+template <> struct KvT<KV_F32> { static constexpr int ESZ = 4, LW = 16; };
+template <> struct KvT<KV_BF16> { static constexpr int ESZ = 2, LW = 16; };
+template <> struct KvT<KV_I8> { static constexpr int ESZ = 1, LW = 8; };
+
+template <int KV, int D, int GT>
+struct Cfg {
+    static constexpr int ESZ = KvT<KV>::ESZ;
+    static constexpr int LW = KvT<KV>::LW;       // bytes per lane per load
+    static constexpr int WORDS = LW / 4;
+    static constexpr int EPL = LW / ESZ;         // row elements per lane
+    static constexpr int LPR = D / EPL;          // lanes sharing one row
+    static constexpr int RPL = kWave / LPR;      // rows per load instruction
+    static constexpr int NLOAD = kBlk / RPL;     // load instructions per tile
+    static constexpr int ROW_BYTES = D * ESZ;
+    static constexpr int TILE_BYTES = kBlk * ROW_BYTES;
+    static constexpr int GTP = GT <= 4 ? 4 : 8;  // LDS stride of one token's logits
+    static constexpr int NV = NLOAD * GT;        // partial dot products per lane per tile
+    static_assert(LPR >= 1 && LPR <= kWave && NLOAD >= 1, "tile shape");
+};
+
+// Number of partitions of sequence s that contain a visible key (1 for an
+// empty context: an item that writes the zero row).
+__device__ __forceinline__ int seq_len(const DecodeArgs& a, int s) {
+    int L = a.context_lens[s];
+    const int cap = a.max_blocks * kBlk;
+    return L < 0 ? 0 : (L > cap ? cap : L);
+}
+__device__ __forceinline__ int first_key(const DecodeArgs& a, int L) {
+    return (a.window > 0 && L > a.window) ? L - a.window : 0;
+}
+__device__ __forceinline__ int num_parts(const DecodeArgs& a, int s) {
+    const int L = seq_len(a, s);
+    if (L == 0 || a.part_tokens == 0) return 1;
+    return (L - 1) / a.part_tokens - first_key(a, L) / a.part_tokens + 1;
+}
+
+template <int WORDS>
+struct Words {
+    uint32_t w[WORDS];
+};
+
+template <int WORDS>
+__device__ __forceinline__ Words<WORDS> load_words(const char* p) {
+    Words<WORDS> r;
+    if constexpr (WORDS == 4) {
+        const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+        r.w[0] = v[0]; r.w[1] = v[1]; r.w[2] = v[2]; r.w[3] = v[3];
+    } else {
+        const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+        r.w[0] = v[0]; r.w[1] = v[1];
+    }
+    return r;
+}
+
+// Row elements of one load as fp32 (INT8: the biased code u = q8 + 128).
+template <int KV, int WORDS>
+__device__ __forceinline__ void widen(const Words<WORDS>& t, float* x) {
+    if constexpr (KV == KV_F32) {
+#pragma unroll
+        for (int i = 0; i < WORDS; ++i) x[i] = __builtin_bit_cast(float, t.w[i]);
+    } else if constexpr (KV == KV_BF16) {
+#pragma unroll
+        for (int i = 0; i < WORDS; ++i) {
+            x[2 * i] = bf16lo(t.w[i]);
+            x[2 * i + 1] = bf16hi(t.w[i]);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < WORDS; ++i) {
+            const uint32_t u = t.w[i] ^ 0x80808080u;
+            x[4 * i + 0] = (float)((u >> 0) & 0xffu);
+            x[4 * i + 1] = (float)((u >> 8) & 0xffu);
+            x[4 * i + 2] = (float)((u >> 16) & 0xffu);
+            x[4 * i + 3] = (float)((u >> 24) & 0xffu);
+        }
+    }
+}
+
+template <int KV, int D, int GT>
+__global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a) {
+    using C = Cfg<KV, D, GT>;
+    constexpr int BUF = (kChunk * C::GTP > kWaves * GT * D) ? kChunk * C::GTP : kWaves * GT * D;
+    __shared__ int s_prefix[kMaxSeqs + 1];
+    __shared__ __attribute__((aligned(16))) float s_buf[BUF];
+    __shared__ float s_red[kWaves][2][C::GTP];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid >> 6;
+    const int B = a.num_seqs;
+
+    // ---- prefix of partition counts (each thread owns up to 8 consecutive sequences)
+    {
+        const int per = (B + kThreads - 1) / kThreads;
+        int cnt[8];
+        int sum = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int s = tid * per + i;
+            cnt[i] = (i < per && s < B) ? num_parts(a, s) : 0;
+            sum += cnt[i];
+        }
+        int* scan = reinterpret_cast<int*>(s_buf);
+        scan[tid] = sum;
+        __syncthreads();
+        for (int off = 1; off < kThreads; off <<= 1) {
+            const int add = tid >= off ? scan[tid - off] : 0;
+            __syncthreads();
+            scan[tid] += add;
+            __syncthreads();
+        }
+        int run = scan[tid] - sum;   // exclusive prefix
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int s = tid * per + i;
+            if (i < per && s < B) s_prefix[s] = run;
+            run += cnt[i];
+        }
+        if (tid == kThreads - 1) s_prefix[B] = scan[tid];
+        __syncthreads();
+    }
+
+    const int HC = a.num_kv_heads * a.head_chunks;
+    const int total = s_prefix[B] * HC;
+    const int row_lane = lane / C::LPR;          // row of this lane inside each load
+    const int col = (lane % C::LPR) * C::EPL;    // first column of this lane
+
+    for (int item = blockIdx.x; item < total; item += gridDim.x) {
+        const int gp = item / HC;
+        const int hc = item - gp * HC;
+        const int g = hc / a.head_chunks;
+        const int hchunk = hc - g * a.head_chunks;
+        int lo_s = 0, hi_s = B - 1;                 // largest s with s_prefix[s] <= gp
+        while (lo_s < hi_s) {
+            const int mid = (lo_s + hi_s + 1) >> 1;
+            if (s_prefix[mid] <= gp) lo_s = mid; else hi_s = mid - 1;
+        }
+        const int s = lo_s;
+        const int nparts = s_prefix[s + 1] - s_prefix[s];
+        const int L = seq_len(a, s);
+        const int lo = first_key(a, L);
+        const int P = a.part_tokens;
+        const int k = (P > 0 ? lo / P : 0) + (gp - s_prefix[s]);
+        const int t0 = P > 0 ? max(lo, k * P) : lo;
+        const int t1 = P > 0 ? min(L, (k + 1) * P) : L;
+        const int h0 = g * a.group + hchunk * GT;   // first query head of this item
+        const int nh = min(GT, a.group - hchunk * GT);
+
+        // ---- query fragment: this lane's columns of each head
+        uint32_t qw[GT][C::WORDS];      // bf16 pairs (bf16 pools)
+        float qf[GT][C::EPL];           // fp32 (fp32 and INT8 pools)
+        float qsum[GT];
+#pragma unroll
+        for (int j = 0; j < GT; ++j) {
+            const int64_t qoff = ((int64_t)s * a.num_q_heads + h0 + j) * D + col;
+            qsum[j] = 0.0f;
+            if constexpr (KV == KV_BF16) {
+                Words<4> t{};
+                if (j < nh) {
+                    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.q) + qoff);
+                    t.w[0] = v[0]; t.w[1] = v[1]; t.w[2] = v[2]; t.w[3] = v[3];
+                }
+#pragma unroll
+                for (int i = 0; i < C::WORDS; ++i) qw[j][i] = t.w[i];
+            } else {
+#pragma unroll
+                for (int e = 0; e < C::EPL; ++e) {
+                    float x = 0.0f;
+                    if (j < nh)
+                        x = a.q_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(a.q)[qoff + e])
+                                     : static_cast<const float*>(a.q)[qoff + e];
+                    qf[j][e] = x;
+                    qsum[j] += x;
+                }
+            }
+        }
+
+        float m_run[GT], l_run[GT], acc[GT][C::EPL], psum[GT];
+#pragma unroll
+        for (int j = 0; j < GT; ++j) {
+            m_run[j] = -INFINITY;
+            l_run[j] = 0.0f;
+            psum[j] = 0.0f;
+#pragma unroll
+            for (int e = 0; e < C::EPL; ++e) acc[j][e] = 0.0f;
+        }
+
+        const int32_t* table = a.block_tables + (int64_t)s * a.max_blocks;
+        for (int c0 = t0; c0 < t1;) {
+            const int c1 = min(t1, (c0 / kChunk + 1) * kChunk);
+            const int fb = c0 / kBlk;
+            const int nblk = (c1 - 1) / kBlk - fb + 1;
+            const int tbase = fb * kBlk;          // token of LDS logit slot 0
+
+            // ---- phase 1: K tiles -> logits
+            for (int b = wave; b < nblk; b += kWaves) {
+                int blk = table[fb + b];
+                const bool blk_ok = blk >= 0 && blk < a.num_blocks;
+                if (!blk_ok) blk = 0;
+                const int64_t tile = (int64_t)blk * a.num_kv_heads + g;
+                const char* kp = a.k_pool + tile * C::TILE_BYTES;
+                float part[C::NV];
+#pragma unroll
+                for (int i = 0; i < C::NLOAD; ++i) {
+                    const Words<C::WORDS> t = load_words<C::WORDS>(kp + (i * kWave + lane) * C::LW);
+                    float ks = 1.0f;
+                    if constexpr (KV == KV_I8) ks = (float)__builtin_bit_cast(_Float16, a.k_scale[tile * kBlk + i * C::RPL + row_lane]);
+                    if constexpr (KV == KV_BF16) {
+#pragma unroll
+                        for (int j = 0; j < GT; ++j) {
+                            float d = 0.0f;
+#pragma unroll
+                            for (int w = 0; w < C::WORDS; ++w)
+                                d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, t.w[w]),
+                                                                    __builtin_bit_cast(bf16x2_t, qw[j][w]), d, false);
+                            part[i * GT + j] = d;
+                        }
+                    } else {
+                        float x[C::EPL];
+                        widen<KV, C::WORDS>(t, x);
+#pragma unroll
+                        for (int j = 0; j < GT; ++j) {
+                            float d = 0.0f;
+#pragma unroll
+                            for (int e = 0; e < C::EPL; ++e) d = fmaf(qf[j][e], x[e], d);
+                            if constexpr (KV == KV_I8) d = (d - 128.0f * qsum[j]) * ks;
+                            part[i * GT + j] = d;
+                        }
+                    }
+                }
+                int base = 0, valid = C::NV;
+                const int n = tbfly<C::NV, C::LPR / 2>(part, lane, base, valid);
+#pragma unroll
+                for (int kk = 0; kk < n; ++kk) {
+                    const int idx = base + kk;
+                    if (kk < valid) {
+                        const int i = idx / GT, j = idx - (idx / GT) * GT;
+                        const int slot = b * kBlk + i * C::RPL + row_lane;
+                        const int tok = tbase + slot;
+                        const bool ok = blk_ok && tok >= c0 && tok < c1;
+                        s_buf[slot * C::GTP + j] = ok ? part[kk] * a.scale_log2 : -INFINITY;
+                    }
+                }
+            }
+            __syncthreads();
+
+            // ---- softmax statistics of the chunk
+            const int T = nblk * kBlk;
+            float mloc[GT];
+#pragma unroll
+            for (int j = 0; j < GT; ++j) mloc[j] = -INFINITY;
+            for (int t = tid; t < T; t += kThreads)
+#pragma unroll
+                for (int j = 0; j < GT; ++j) mloc[j] = fmaxf(mloc[j], s_buf[t * C::GTP + j]);
+#pragma unroll
+            for (int j = 0; j < GT; ++j) {
+                mloc[j] = group_max<kWave>(mloc[j]);
+                if (lane == 0) s_red[wave][0][j] = mloc[j];
+            }
+            __syncthreads();
+            float m_new[GT], lloc[GT];
+#pragma unroll
+            for (int j = 0; j < GT; ++j) {
+                float m = m_run[j];
+#pragma unroll
+                for (int w = 0; w < kWaves; ++w) m = fmaxf(m, s_red[w][0][j]);
+                m_new[j] = m;
+                lloc[j] = 0.0f;
+            }
+            for (int t = tid; t < T; t += kThreads)
+#pragma unroll
+                for (int j = 0; j < GT; ++j) {
+                    const float x = s_buf[t * C::GTP + j];
+                    const float p = (x == -INFINITY) ? 0.0f : fast_exp2(x - m_new[j]);
+                    s_buf[t * C::GTP + j] = p;
+                    lloc[j] += p;
+                }
+#pragma unroll
+            for (int j = 0; j < GT; ++j) {
+                lloc[j] = group_sum<kWave>(lloc[j]);
+                if (lane == 0) s_red[wave][1][j] = lloc[j];
+            }
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < GT; ++j) {
+                float l = 0.0f;
+#pragma unroll
+                for (int w = 0; w < kWaves; ++w) l += s_red[w][1][j];
+                const float alpha = (m_run[j] == -INFINITY) ? 0.0f : fast_exp2(m_run[j] - m_new[j]);
+                l_run[j] = l_run[j] * alpha + l;
+                m_run[j] = m_new[j];
+                psum[j] *= alpha;
+#pragma unroll
+                for (int e = 0; e < C::EPL; ++e) acc[j][e] *= alpha;
+            }
+
+            // ---- phase 2: V tiles, p * v
+            for (int b = wave; b < nblk; b += kWaves) {
+                int blk = table[fb + b];
+                const bool blk_ok = blk >= 0 && blk < a.num_blocks;
+                if (!blk_ok) blk = 0;
+                const int64_t tile = (int64_t)blk * a.num_kv_heads + g;
+                const char* vp = a.v_pool + tile * C::TILE_BYTES;
+                const bool full = blk_ok && tbase + b * kBlk >= c0 && tbase + (b + 1) * kBlk <= c1;
+#pragma unroll
+                for (int i = 0; i < C::NLOAD; ++i) {
+                    Words<C::WORDS> t = load_words<C::WORDS>(vp + (i * kWave + lane) * C::LW);
+                    const int slot = b * kBlk + i * C::RPL + row_lane;
+                    if (!full) {
+                        const int tok = tbase + slot;
+                        const bool ok = blk_ok && tok >= c0 && tok < c1;
+#pragma unroll
+                        for (int w = 0; w < C::WORDS; ++w) t.w[w] = ok ? t.w[w] : 0u;
+                    }
+                    float p[C::GTP];
+                    const f32x4_t p0 = *reinterpret_cast<const f32x4_t*>(&s_buf[slot * C::GTP]);
+                    p[0] = p0[0]; p[1] = p0[1]; p[2] = p0[2]; p[3] = p0[3];
+                    if constexpr (C::GTP == 8) {
+                        const f32x4_t p1 = *reinterpret_cast<const f32x4_t*>(&s_buf[slot * C::GTP + 4]);
+                        p[4] = p1[0]; p[5] = p1[1]; p[6] = p1[2]; p[7] = p1[3];
+                    }
+                    if constexpr (KV == KV_I8) {
+                        const float vs = (float)__builtin_bit_cast(_Float16, a.v_scale[tile * kBlk + i * C::RPL + row_lane]);
+#pragma unroll
+                        for (int j = 0; j < GT; ++j) {
+                            p[j] = (full || (blk_ok && tbase + slot >= c0 && tbase + slot < c1)) ? p[j] * vs : 0.0f;
+                            psum[j] += p[j];
+                        }
+                    }
+                    float x[C::EPL];
+                    widen<KV, C::WORDS>(t, x);
+#pragma unroll
+                    for (int j = 0; j < GT; ++j)
+#pragma unroll
+                        for (int e = 0; e < C::EPL; ++e) acc[j][e] = fmaf(p[j], x[e], acc[j][e]);
+                }
+            }
+            __syncthreads();
+            c0 = c1;
+        }
+
+        // ---- combine the lanes of each column, then the waves
+        if constexpr (KV == KV_I8) {
+#pragma unroll
+            for (int j = 0; j < GT; ++j)
+#pragma unroll
+                for (int e = 0; e < C::EPL; ++e) acc[j][e] -= 128.0f * psum[j];
+        }
+#pragma unroll
+        for (int j = 0; j < GT; ++j)
+#pragma unroll
+            for (int e = 0; e < C::EPL; ++e) {
+                float v = acc[j][e];
+#pragma unroll
+                for (int off = C::LPR; off < kWave; off <<= 1) v += __shfl_xor(v, off, kWave);
+                acc[j][e] = v;
+            }
+        if (lane < C::LPR) {
+#pragma unroll
+            for (int j = 0; j < GT; ++j)
+#pragma unroll
+                for (int e = 0; e < C::EPL; ++e) s_buf[(wave * GT + j) * D + col + e] = acc[j][e];
+        }
+        __syncthreads();
+        for (int idx = tid; idx < GT * D; idx += kThreads) {
+            const int j = idx / D, d = idx - (idx / D) * D;
+            if (j >= nh) continue;
+            float o = 0.0f;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) o += s_buf[(w * GT + j) * D + d];
+            const int h = h0 + j;
+            float mj = 0.0f, lj = 0.0f;
+#pragma unroll
+            for (int jj = 0; jj < GT; ++jj)
+                if (jj == j) { mj = m_run[jj]; lj = l_run[jj]; }
+            if (nparts == 1) {
+                const float r = lj > 0.0f ? o / lj : 0.0f;
+                const int64_t oi = ((int64_t)s * a.num_q_heads + h) * D + d;
+                if (a.out_bf16) static_cast<uint16_t*>(a.out)[oi] = f32_to_bf16(r);
+                else static_cast<float*>(a.out)[oi] = r;
+            } else {
+                const int64_t pi = ((int64_t)s * a.num_q_heads + h) * a.max_parts + k;
+                a.part_o[pi * D + d] = o;
+                if (d == 0) {
+                    a.part_ml[pi * 2] = mj;
+                    a.part_ml[pi * 2 + 1] = lj;
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// Merge the partitions of every (sequence, head) with more than one:
+// out = sum_k 2^(m_k - M) o_k / sum_k 2^(m_k - M) l_k, M = max_k m_k.
+template <int D>
+__global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecodeArgs a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int pair = blockIdx.x * kWaves + (threadIdx.x >> 6);
+    if (pair >= a.num_seqs * a.num_q_heads) return;
+    const int s = pair / a.num_q_heads;
+    const int n = num_parts(a, s);
+    if (n <= 1) return;
+    const int L = seq_len(a, s);
+    const int k0 = first_key(a, L) / a.part_tokens;
+    const float* ml = a.part_ml + (int64_t)pair * a.max_parts * 2;
+    const float* po = a.part_o + (int64_t)pair * a.max_parts * D;
+
+    float M = -INFINITY;
+    for (int k = lane; k < n; k += kWave) M = fmaxf(M, ml[(k0 + k) * 2]);
+    M = group_max<kWave>(M);
+    float den = 0.0f;
+    for (int k = lane; k < n; k += kWave) den += fast_exp2(ml[(k0 + k) * 2] - M) * ml[(k0 + k) * 2 + 1];
+    den = group_sum<kWave>(den);
+    constexpr int E = D / kWave;
+    float o[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[e] = 0.0f;
+    for (int k = 0; k < n; ++k) {
+        const float w = fast_exp2(ml[(k0 + k) * 2] - M);
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[e] = fmaf(w, po[(int64_t)(k0 + k) * D + lane * E + e], o[e]);
+    }
+    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int64_t oi = (int64_t)pair * D + lane * E + e;
+        const float r = o[e] * inv;
+        if (a.out_bf16) static_cast<uint16_t*>(a.out)[oi] = f32_to_bf16(r);
+        else static_cast<float*>(a.out)[oi] = r;
+    }
+}
+
+// ---------------------------------------------------------------- host side
+using PartKernel = void (*)(DecodeArgs);
+
+template <int KV, int D>
+static PartKernel pick_gt(int gt) {
+    switch (gt) {
+    case 1: return decode_partition_kernel<KV, D, 1>;
+    case 2: return decode_partition_kernel<KV, D, 2>;
+    case 3: return decode_partition_kernel<KV, D, 3>;
+    case 4: return decode_partition_kernel<KV, D, 4>;
+    case 5: return decode_partition_kernel<KV, D, 5>;
+    case 6: return decode_partition_kernel<KV, D, 6>;
+    case 7: return decode_partition_kernel<KV, D, 7>;
+    default: return decode_partition_kernel<KV, D, 8>;
+    }
+}
+
+static PartKernel pick(KvKind kv, int D, int gt) {
+    if (kv == KV_F32) return D == 64 ? pick_gt<KV_F32, 64>(gt) : pick_gt<KV_F32, 128>(gt);
+    if (kv == KV_BF16) return D == 64 ? pick_gt<KV_BF16, 64>(gt) : pick_gt<KV_BF16, 128>(gt);
+    return D == 64 ? pick_gt<KV_I8, 64>(gt) : pick_gt<KV_I8, 128>(gt);
+}
+
+int32_t decode_max_partitions(int32_t max_blocks_per_seq, int32_t block_size, int32_t partition_size) {
+    if (partition_size <= 0) return 0;
+    const int64_t cap = (int64_t)max_blocks_per_seq * block_size;
+    const int64_t n = (cap + partition_size - 1) / partition_size;
+    return n <= 1 ? 0 : (int32_t)n;
+}
+
+size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                              int32_t max_partitions) {
+    if (max_partitions <= 0) return 0;
+    const size_t slots = (size_t)num_seqs * num_q_heads * max_partitions;
+    const size_t ml = (slots * 2 * sizeof(float) + 255) & ~(size_t)255;
+    return ml + slots * head_dim * sizeof(float);
+}
+
+hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
+    const int G = L.num_q_heads / L.num_kv_heads;
+    const int chunks = (G + kMaxGroup - 1) / kMaxGroup;
+    const int gt = (G + chunks - 1) / chunks;
+    const int max_parts = decode_max_partitions(L.max_blocks_per_seq, L.block_size, L.partition_size);
+    const bool merge = max_parts > 1;
+
+    DecodeArgs a;
+    a.q = L.q;
+    a.out = L.out;
+    a.k_pool = static_cast<const char*>(L.k_pool);
+    a.v_pool = static_cast<const char*>(L.v_pool);
+    a.k_scale = L.k_scale;
+    a.v_scale = L.v_scale;
+    a.num_q_heads = L.num_q_heads;
+    a.num_kv_heads = L.num_kv_heads;
+    a.group = G;
+    a.head_chunks = chunks;
+    a.num_blocks = L.num_blocks;
+    a.max_blocks = L.max_blocks_per_seq;
+    a.window = L.window;
+    a.part_tokens = merge ? L.partition_size : 0;
+    a.max_parts = merge ? max_parts : 1;
+    a.scale_log2 = L.softmax_scale * kLog2e;
+    a.q_bf16 = L.q_bf16;
+    a.out_bf16 = L.out_bf16;
+
+    PartKernel kern = pick(L.kv, L.head_dim, gt);
+    static thread_local PartKernel occ_kern = nullptr;
+    static thread_local int occ = 0;
+    if (occ_kern != kern) {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(kern), kThreads, 0) != hipSuccess || n < 1) n = 1;
+        occ = n;
+        occ_kern = kern;
+    }
+    const int64_t resident = (int64_t)device_cu_count() * occ;
+    const int64_t per_seq_items = (int64_t)(merge ? max_parts : 1) * L.num_kv_heads * chunks;
+
+    const size_t slots_total = (size_t)L.num_seqs * L.num_q_heads * (merge ? max_parts : 0);
+    float* ml_base = static_cast<float*>(L.workspace);
+    float* o_base = merge ? reinterpret_cast<float*>(static_cast<char*>(L.workspace) +
+                                                     ((slots_total * 2 * sizeof(float) + 255) & ~(size_t)255))
+                          : nullptr;
+
+    for (int32_t s0 = 0; s0 < L.num_seqs; s0 += kMaxSeqs) {
+        const int32_t n = std::min<int32_t>(kMaxSeqs, L.num_seqs - s0);
+        DecodeArgs b = a;
+        b.num_seqs = n;
+        const int64_t qoff = (int64_t)s0 * L.num_q_heads * L.head_dim;
+        b.q = static_cast<const char*>(L.q) + qoff * (L.q_bf16 ? 2 : 4);
+        b.out = static_cast<char*>(L.out) + qoff * (L.out_bf16 ? 2 : 4);
+        b.block_tables = L.block_tables + (int64_t)s0 * L.max_blocks_per_seq;
+        b.context_lens = L.context_lens + s0;
+        b.part_ml = merge ? ml_base + (int64_t)s0 * L.num_q_heads * max_parts * 2 : nullptr;
+        b.part_o = merge ? o_base + (int64_t)s0 * L.num_q_heads * max_parts * L.head_dim : nullptr;
+        const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(resident, (int64_t)n * per_seq_items));
+        hipError_t e = launch(kern, dim3((unsigned)grid), dim3(kThreads), 0, stream, b);
+        if (e != hipSuccess) return e;
+        if (merge) {
+            if (L.split_event) {
+                e = hipEventRecord(L.split_event, stream);
+                if (e != hipSuccess) return e;
+            }
+            const int64_t pairs = (int64_t)n * L.num_q_heads;
+            const unsigned mg = (unsigned)((pairs + kWaves - 1) / kWaves);
+            e = L.head_dim == 64 ? launch(decode_merge_kernel<64>, dim3(mg), dim3(kThreads), 0, stream, b)
+                                 : launch(decode_merge_kernel<128>, dim3(mg), dim3(kThreads), 0, stream, b);
+            if (e != hipSuccess) return e;
+        }
+    }
+    return hipSuccess;
+}
+
+}  // namespace pkv

@@ -1,0 +1,335 @@
+// pkv_api.cpp -- the C ABI of libpagedkv (declared in include/pagedkv.h):
+// argument validation, error reporting and dispatch to the kernel launchers.
+// Nothing is enqueued unless every host-visible argument is valid.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "pagedkv.h"
+#include "pkv_internal.h"
+
+namespace {
+
+thread_local std::string g_error;
+thread_local hipEvent_t g_split_event = nullptr;
+
+int fail(int status, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_error = buf;
+    return status;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(PKV_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+const char* dtype_name(int32_t t) {
+    switch (t) {
+    case PKV_F32: return "F32";
+    case PKV_BF16: return "BF16";
+    case PKV_I8: return "I8";
+    default: return "invalid";
+    }
+}
+
+int check_cache(const pkv_cache_desc* c) {
+    if (!c) return fail(PKV_EINVAL, "cache descriptor is NULL");
+    if (c->num_blocks <= 0) return fail(PKV_EINVAL, "num_blocks must be > 0 (got %d)", c->num_blocks);
+    if (c->num_kv_heads <= 0) return fail(PKV_EINVAL, "num_kv_heads must be > 0 (got %d)", c->num_kv_heads);
+    if (c->block_size <= 0 || c->head_dim <= 0)
+        return fail(PKV_EINVAL, "block_size and head_dim must be > 0");
+    if (c->block_size != 16) return fail(PKV_EUNSUPPORTED, "block_size %d unsupported (16 only)", c->block_size);
+    if (c->head_dim != 64 && c->head_dim != 128)
+        return fail(PKV_EUNSUPPORTED, "head_dim %d unsupported (64 or 128)", c->head_dim);
+    if (c->kv_dtype != PKV_F32 && c->kv_dtype != PKV_BF16 && c->kv_dtype != PKV_I8)
+        return fail(PKV_EINVAL, "kv_dtype %d is not a pkv_dtype", c->kv_dtype);
+    if ((int64_t)c->num_blocks * c->block_size > INT32_MAX)
+        return fail(PKV_EUNSUPPORTED, "num_blocks * block_size exceeds the int32 slot range");
+    return PKV_OK;
+}
+
+bool validate_env() {
+    static const bool on = [] {
+        const char* v = std::getenv("PKV_VALIDATE");
+        return v && *v && std::strcmp(v, "0") != 0;
+    }();
+    return on;
+}
+
+template <typename T>
+int copy_to_host(std::vector<T>& dst, const T* src, size_t n, hipStream_t stream) {
+    dst.resize(n);
+    if (n == 0) return PKV_OK;
+    hipError_t e = hipMemcpyAsync(dst.data(), src, n * sizeof(T), hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    return e == hipSuccess ? PKV_OK : hip_fail(e, "PKV_VALIDATE copy");
+}
+
+// PKV_VALIDATE=1: check device-resident tables and lengths on the host.
+int validate_tables(const pkv_cache_desc* c, int32_t num_seqs, const int32_t* block_tables,
+                    int32_t max_blocks, const int32_t* lens, const int32_t* cu, hipStream_t stream) {
+    std::vector<int32_t> L, T, CU;
+    int rc = copy_to_host(L, lens, (size_t)num_seqs, stream);
+    if (rc == PKV_OK) rc = copy_to_host(T, block_tables, (size_t)num_seqs * max_blocks, stream);
+    if (rc == PKV_OK && cu) rc = copy_to_host(CU, cu, (size_t)num_seqs + 1, stream);
+    if (rc != PKV_OK) return rc;
+    if (cu && CU[0] != 0) return fail(PKV_EINVAL, "cu_q_lens[0] = %d, expected 0", CU[0]);
+    for (int32_t s = 0; s < num_seqs; ++s) {
+        const int64_t cap = (int64_t)max_blocks * c->block_size;
+        if (L[s] < 0 || L[s] > cap)
+            return fail(PKV_EINVAL, "length %d of sequence %d outside [0, %lld]", L[s], s, (long long)cap);
+        if (cu) {
+            const int32_t C = CU[s + 1] - CU[s];
+            if (C < 0 || C > L[s]) return fail(PKV_EINVAL, "chunk length %d of sequence %d outside [0, %d]", C, s, L[s]);
+        }
+        const int32_t used = (L[s] + c->block_size - 1) / c->block_size;
+        for (int32_t b = 0; b < used; ++b) {
+            const int32_t id = T[(size_t)s * max_blocks + b];
+            if (id < 0 || id >= c->num_blocks)
+                return fail(PKV_EINVAL, "block_tables[%d][%d] = %d outside [0, %d)", s, b, id, c->num_blocks);
+        }
+    }
+    return PKV_OK;
+}
+
+}  // namespace
+
+namespace pkv {
+int device_cu_count() {
+    static thread_local int cached_dev = -1;
+    static thread_local int cached_cus = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (dev != cached_dev) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        cached_dev = dev;
+        cached_cus = cus;
+    }
+    return cached_cus;
+}
+}  // namespace pkv
+
+extern "C" {
+
+const char* pkv_last_error(void) { return g_error.c_str(); }
+
+const char* pkv_version(void) { return "libpagedkv 0.1 (gfx950)"; }
+
+int pkv_profile_set_decode_split_event(void* hip_event) {
+    g_split_event = static_cast<hipEvent_t>(hip_event);
+    return PKV_OK;
+}
+
+int kv_cache_write(const pkv_cache_desc* cache, const void* k, const void* v, int32_t in_dtype,
+                   int64_t token_stride, const int32_t* slot_mapping, int32_t num_tokens,
+                   void* k_pool, void* v_pool, void* k_scale, void* v_scale, void* stream) {
+    g_error.clear();
+    int rc = check_cache(cache);
+    if (rc != PKV_OK) return rc;
+    if (num_tokens < 0) return fail(PKV_EINVAL, "num_tokens must be >= 0 (got %d)", num_tokens);
+    if (in_dtype != PKV_F32 && in_dtype != PKV_BF16)
+        return fail(in_dtype == PKV_I8 ? PKV_EUNSUPPORTED : PKV_EINVAL, "input dtype %s unsupported (F32 or BF16)",
+                    dtype_name(in_dtype));
+    const bool quantise = cache->kv_dtype == PKV_I8;
+    if (!quantise && cache->kv_dtype != in_dtype)
+        return fail(PKV_EUNSUPPORTED, "writing %s vectors into a %s pool is unsupported", dtype_name(in_dtype),
+                    dtype_name(cache->kv_dtype));
+    if (quantise && (!k_scale || !v_scale)) return fail(PKV_EINVAL, "INT8 pools need k_scale and v_scale");
+    if (!quantise && (k_scale || v_scale)) return fail(PKV_EINVAL, "k_scale/v_scale must be NULL for %s pools",
+                                                       dtype_name(cache->kv_dtype));
+    if (num_tokens == 0) return PKV_OK;
+    if (!k || !v || !slot_mapping || !k_pool || !v_pool) return fail(PKV_EINVAL, "NULL tensor pointer");
+    const int64_t esz = in_dtype == PKV_BF16 ? 2 : 4;
+    const int64_t row = (int64_t)cache->num_kv_heads * cache->head_dim;
+    if (token_stride < row) return fail(PKV_EINVAL, "token_stride %lld < num_kv_heads * head_dim = %lld",
+                                        (long long)token_stride, (long long)row);
+    if ((token_stride * esz) % 16 != 0) return fail(PKV_EINVAL, "token_stride * element size must be a multiple of 16 bytes");
+    if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16))
+        return fail(PKV_EINVAL, "k, v and the pools must be 16-byte aligned");
+    if (quantise && (!aligned(k_scale, 2) || !aligned(v_scale, 2))) return fail(PKV_EINVAL, "scale pools must be 2-byte aligned");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (validate_env()) {
+        std::vector<int32_t> slots;
+        rc = copy_to_host(slots, slot_mapping, (size_t)num_tokens, st);
+        if (rc != PKV_OK) return rc;
+        const int64_t nslots = (int64_t)cache->num_blocks * cache->block_size;
+        std::vector<char> seen((size_t)nslots, 0);
+        for (int32_t t = 0; t < num_tokens; ++t) {
+            if (slots[t] < 0) continue;
+            if (slots[t] >= nslots) return fail(PKV_EINVAL, "slot_mapping[%d] = %d outside [0, %lld)", t, slots[t], (long long)nslots);
+            if (seen[slots[t]]++) return fail(PKV_EINVAL, "slot %d written twice", slots[t]);
+        }
+    }
+    pkv::KvWriteLaunch L;
+    L.k = k;
+    L.v = v;
+    L.in_bf16 = in_dtype == PKV_BF16;
+    L.quantise = quantise;
+    L.token_stride = token_stride;
+    L.slot_mapping = slot_mapping;
+    L.num_tokens = num_tokens;
+    L.num_blocks = cache->num_blocks;
+    L.block_size = cache->block_size;
+    L.num_kv_heads = cache->num_kv_heads;
+    L.head_dim = cache->head_dim;
+    L.k_pool = k_pool;
+    L.v_pool = v_pool;
+    L.k_scale = k_scale;
+    L.v_scale = v_scale;
+    const hipError_t e = pkv::launch_kv_write(L, st);
+    return e == hipSuccess ? PKV_OK : hip_fail(e, "kv_cache_write launch");
+}
+
+size_t paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                             int32_t max_blocks_per_seq, int32_t block_size,
+                                             int32_t partition_size) {
+    if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0 || max_blocks_per_seq <= 0 || block_size <= 0 ||
+        partition_size < 0)
+        return 0;
+    const int32_t np = pkv::decode_max_partitions(max_blocks_per_seq, block_size, partition_size);
+    return pkv::decode_workspace_bytes(num_seqs, num_q_heads, head_dim, np);
+}
+
+int paged_attention_decode(const pkv_cache_desc* cache, const void* q, int32_t q_dtype, void* out,
+                           int32_t out_dtype, int32_t num_seqs, int32_t num_q_heads, const void* k_pool,
+                           const void* v_pool, const void* k_scale, const void* v_scale,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, float softmax_scale, int32_t sliding_window,
+                           int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
+    g_error.clear();
+    int rc = check_cache(cache);
+    if (rc != PKV_OK) return rc;
+    if (num_seqs < 0) return fail(PKV_EINVAL, "num_seqs must be >= 0 (got %d)", num_seqs);
+    if (num_q_heads <= 0 || num_q_heads % cache->num_kv_heads != 0)
+        return fail(PKV_EINVAL, "num_q_heads %d is not a positive multiple of num_kv_heads %d", num_q_heads,
+                    cache->num_kv_heads);
+    if (max_blocks_per_seq <= 0) return fail(PKV_EINVAL, "max_blocks_per_seq must be > 0");
+    if ((int64_t)max_blocks_per_seq * cache->block_size > INT32_MAX)
+        return fail(PKV_EUNSUPPORTED, "max_blocks_per_seq * block_size exceeds int32");
+    if (sliding_window < 0) return fail(PKV_EINVAL, "sliding_window must be >= 0");
+    if (!std::isfinite(softmax_scale) || softmax_scale < 0.0f)
+        return fail(PKV_EINVAL, "softmax_scale must be finite and >= 0");
+    if (partition_size < 0 || partition_size % cache->block_size != 0)
+        return fail(PKV_EINVAL, "partition_size %d must be 0 or a positive multiple of block_size", partition_size);
+    const int32_t kv = cache->kv_dtype;
+    const bool q_ok = (kv == PKV_BF16 && q_dtype == PKV_BF16) || (kv == PKV_F32 && q_dtype == PKV_F32) ||
+                      (kv == PKV_I8 && (q_dtype == PKV_BF16 || q_dtype == PKV_F32));
+    if (q_dtype != PKV_F32 && q_dtype != PKV_BF16) return fail(PKV_EINVAL, "q_dtype %d is not F32 or BF16", q_dtype);
+    if (!q_ok) return fail(PKV_EUNSUPPORTED, "q dtype %s with a %s pool is unsupported", dtype_name(q_dtype), dtype_name(kv));
+    if (out_dtype != PKV_F32 && out_dtype != PKV_BF16) return fail(PKV_EUNSUPPORTED, "out_dtype must be F32 or BF16");
+    if (kv == PKV_I8 && (!k_scale || !v_scale)) return fail(PKV_EINVAL, "INT8 pools need k_scale and v_scale");
+    if (kv != PKV_I8 && (k_scale || v_scale)) return fail(PKV_EINVAL, "k_scale/v_scale must be NULL for %s pools", dtype_name(kv));
+    if (num_seqs == 0) return PKV_OK;
+    if (!q || !out || !k_pool || !v_pool || !block_tables || !context_lens) return fail(PKV_EINVAL, "NULL tensor pointer");
+    if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16))
+        return fail(PKV_EINVAL, "q, out and the pools must be 16-byte aligned");
+    const size_t need = paged_attention_decode_workspace_size(num_seqs, num_q_heads, cache->head_dim,
+                                                              max_blocks_per_seq, cache->block_size, partition_size);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(PKV_EWORKSPACE, "workspace of %zu bytes needed (got %zu)", need, workspace ? workspace_bytes : (size_t)0);
+    if (need > 0 && !aligned(workspace, 256)) return fail(PKV_EINVAL, "workspace must be 256-byte aligned");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (validate_env()) {
+        rc = validate_tables(cache, num_seqs, block_tables, max_blocks_per_seq, context_lens, nullptr, st);
+        if (rc != PKV_OK) return rc;
+    }
+    pkv::DecodeLaunch L;
+    L.q = q;
+    L.q_bf16 = q_dtype == PKV_BF16;
+    L.out = out;
+    L.out_bf16 = out_dtype == PKV_BF16;
+    L.num_seqs = num_seqs;
+    L.num_q_heads = num_q_heads;
+    L.num_kv_heads = cache->num_kv_heads;
+    L.head_dim = cache->head_dim;
+    L.block_size = cache->block_size;
+    L.num_blocks = cache->num_blocks;
+    L.kv = kv == PKV_F32 ? pkv::KV_F32 : kv == PKV_BF16 ? pkv::KV_BF16 : pkv::KV_I8;
+    L.k_pool = k_pool;
+    L.v_pool = v_pool;
+    L.k_scale = static_cast<const uint16_t*>(k_scale);
+    L.v_scale = static_cast<const uint16_t*>(v_scale);
+    L.block_tables = block_tables;
+    L.max_blocks_per_seq = max_blocks_per_seq;
+    L.context_lens = context_lens;
+    L.softmax_scale = softmax_scale;
+    L.window = sliding_window;
+    L.partition_size = partition_size;
+    L.workspace = workspace;
+    L.split_event = g_split_event;
+    const hipError_t e = pkv::launch_decode(L, st);
+    return e == hipSuccess ? PKV_OK : hip_fail(e, "paged_attention_decode launch");
+}
+
+int paged_attention_prefill_chunk(const pkv_cache_desc* cache, const void* q, int32_t q_dtype, void* out,
+                                  int32_t out_dtype, const int32_t* cu_q_lens, int32_t num_seqs,
+                                  int32_t max_q_len, int32_t num_q_heads, const void* k_pool,
+                                  const void* v_pool, const int32_t* block_tables,
+                                  int32_t max_blocks_per_seq, const int32_t* seq_lens, float softmax_scale,
+                                  int32_t sliding_window, void* stream) {
+    g_error.clear();
+    int rc = check_cache(cache);
+    if (rc != PKV_OK) return rc;
+    if (num_seqs < 0 || max_q_len < 0) return fail(PKV_EINVAL, "num_seqs and max_q_len must be >= 0");
+    if (num_q_heads <= 0 || num_q_heads % cache->num_kv_heads != 0)
+        return fail(PKV_EINVAL, "num_q_heads %d is not a positive multiple of num_kv_heads %d", num_q_heads,
+                    cache->num_kv_heads);
+    if (max_blocks_per_seq <= 0) return fail(PKV_EINVAL, "max_blocks_per_seq must be > 0");
+    if ((int64_t)max_blocks_per_seq * cache->block_size > INT32_MAX)
+        return fail(PKV_EUNSUPPORTED, "max_blocks_per_seq * block_size exceeds int32");
+    if (sliding_window < 0) return fail(PKV_EINVAL, "sliding_window must be >= 0");
+    if (!std::isfinite(softmax_scale) || softmax_scale < 0.0f)
+        return fail(PKV_EINVAL, "softmax_scale must be finite and >= 0");
+    if (q_dtype != PKV_BF16) return fail(q_dtype == PKV_F32 ? PKV_EUNSUPPORTED : PKV_EINVAL, "prefill needs BF16 q");
+    if (cache->kv_dtype != PKV_BF16) return fail(PKV_EUNSUPPORTED, "prefill needs a BF16 pool (got %s)", dtype_name(cache->kv_dtype));
+    if (out_dtype != PKV_F32 && out_dtype != PKV_BF16) return fail(PKV_EUNSUPPORTED, "out_dtype must be F32 or BF16");
+    if ((int64_t)max_q_len * (num_q_heads / cache->num_kv_heads) > INT32_MAX / 2)
+        return fail(PKV_EUNSUPPORTED, "max_q_len too large");
+    if (num_seqs == 0 || max_q_len == 0) return PKV_OK;
+    if (!q || !out || !cu_q_lens || !k_pool || !v_pool || !block_tables || !seq_lens)
+        return fail(PKV_EINVAL, "NULL tensor pointer");
+    if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16))
+        return fail(PKV_EINVAL, "q, out and the pools must be 16-byte aligned");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (validate_env()) {
+        rc = validate_tables(cache, num_seqs, block_tables, max_blocks_per_seq, seq_lens, cu_q_lens, st);
+        if (rc != PKV_OK) return rc;
+    }
+    pkv::PrefillLaunch L;
+    L.q = q;
+    L.out = out;
+    L.out_bf16 = out_dtype == PKV_BF16;
+    L.cu_q_lens = cu_q_lens;
+    L.num_seqs = num_seqs;
+    L.max_q_len = max_q_len;
+    L.num_q_heads = num_q_heads;
+    L.num_kv_heads = cache->num_kv_heads;
+    L.head_dim = cache->head_dim;
+    L.block_size = cache->block_size;
+    L.num_blocks = cache->num_blocks;
+    L.k_pool = k_pool;
+    L.v_pool = v_pool;
+    L.block_tables = block_tables;
+    L.max_blocks_per_seq = max_blocks_per_seq;
+    L.seq_lens = seq_lens;
+    L.softmax_scale = softmax_scale;
+    L.window = sliding_window;
+    const hipError_t e = pkv::launch_prefill(L, st);
+    return e == hipSuccess ? PKV_OK : hip_fail(e, "paged_attention_prefill_chunk launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,124 @@
+"""Helpers for the GPU parity tests: device pools for a seeded workload, the
+library calls, and the comparison rules.
+
+Tolerances (GPU vs the fp64 oracle):
+  * fp32 inputs: max abs error <= 1e-5;
+  * bf16 / INT8 inputs, fp32 accumulation: max abs error <= 2e-3 and, per
+    output vector (one token and head), max|gpu - ref| / max|ref| <= 1e-2.
+    Elementwise relative error is unbounded where ref is near 0, so the
+    relative bound is taken per vector.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import paged_kv_cache_235_amd as pkv
+
+ABS_F32 = 1e-5
+ABS_BF16 = 2e-3
+REL_BF16 = 1e-2
+
+_TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8}
+
+
+def device():
+    return torch.device("cuda", 0)
+
+
+def alloc_pools(case, dev, kv_dtype=None):
+    """Pools in the library layout, poisoned: NaN (fp32/bf16), -128 codes and NaN scales (INT8)."""
+    kv_dtype = kv_dtype or case.kv_dtype
+    shape = (case.num_blocks, case.num_kv_heads, case.block_size, case.head_dim)
+    t = _TORCH[kv_dtype]
+    pools = {}
+    if kv_dtype == "i8":
+        pools["k"] = torch.full(shape, -128, dtype=t, device=dev)
+        pools["v"] = torch.full(shape, -128, dtype=t, device=dev)
+        pools["ks"] = torch.full(shape[:3], float("nan"), dtype=torch.float16, device=dev)
+        pools["vs"] = torch.full(shape[:3], float("nan"), dtype=torch.float16, device=dev)
+    else:
+        pools["k"] = torch.full(shape, float("nan"), dtype=t, device=dev)
+        pools["v"] = torch.full(shape, float("nan"), dtype=t, device=dev)
+        pools["ks"] = pools["vs"] = None
+    return pools
+
+
+def write_tokens(case, pools, dev, which="all", batch_tokens=1 << 16):
+    """Write tokens of every sequence through kv_cache_write.
+    which: 'context' (before this step), 'new' (this step's) or 'all'."""
+    ks, vs, ss, n = [], [], [], 0
+
+    def flush():
+        nonlocal ks, vs, ss, n
+        if not ks:
+            return
+        k = torch.cat(ks)
+        v = torch.cat(vs)
+        slots = torch.from_numpy(np.concatenate(ss)).to(dev)
+        pkv.kv_cache_write(k, v, slots, pools["k"], pools["v"], pools["ks"], pools["vs"])
+        ks, vs, ss, n = [], [], [], 0
+
+    for s in range(case.num_seqs):
+        if which == "context":
+            p0, p1 = case.context_range(s)
+        elif which == "new":
+            p0, p1 = case.new_range(s)
+        else:
+            p0, p1 = 0, int(case.seq_lens[s])
+        for a in range(p0, p1, batch_tokens):
+            b = min(p1, a + batch_tokens)
+            ks.append(case.kv("k", s, a, b, dev))
+            vs.append(case.kv("v", s, a, b, dev))
+            ss.append(case.slots(s, a, b))
+            n += b - a
+            if n >= batch_tokens:
+                flush()
+    flush()
+
+
+def tables(case, dev):
+    return (torch.from_numpy(case.block_tables).to(dev),
+            torch.from_numpy(case.seq_lens).to(dev),
+            torch.from_numpy(case.cu_q_lens).to(dev))
+
+
+def run_decode(case, pools, dev, **kw):
+    bt, lens, _ = tables(case, dev)
+    q = case.q(dev)
+    return pkv.paged_attention_decode(q, pools["k"], pools["v"], bt, lens, case.softmax_scale,
+                                      sliding_window=case.window,
+                                      partition_size=kw.pop("partition_size", case.partition_size),
+                                      k_scale=pools["ks"], v_scale=pools["vs"], **kw)
+
+
+def run_prefill(case, pools, dev, **kw):
+    bt, lens, cu = tables(case, dev)
+    q = case.q(dev)
+    return pkv.paged_attention_prefill_chunk(q, cu, lens, pools["k"], pools["v"], bt, case.max_q_len,
+                                             case.softmax_scale, sliding_window=case.window, **kw)
+
+
+def assert_close(got: torch.Tensor, ref: np.ndarray, dtype: str, what: str = ""):
+    g = got.detach().float().cpu().double().numpy().reshape(ref.shape)
+    assert np.isfinite(g).all(), f"{what}: non-finite output"
+    err = np.abs(g - ref)
+    if dtype == "f32":
+        assert err.max() <= ABS_F32, f"{what}: max abs error {err.max():.3e} > {ABS_F32}"
+        return err.max()
+    assert err.max() <= ABS_BF16, f"{what}: max abs error {err.max():.3e} > {ABS_BF16}"
+    d = ref.shape[-1]
+    e = err.reshape(-1, d).max(1)
+    r = np.abs(ref).reshape(-1, d).max(1)
+    nz = r > 0
+    rel = (e[nz] / r[nz]).max() if nz.any() else 0.0
+    assert rel <= REL_BF16, f"{what}: per-vector relative error {rel:.3e} > {REL_BF16}"
+    assert (e[~nz] <= ABS_BF16).all()
+    return err.max()
+
+
+def bf16_ulp(x: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 numbers at |x| (8 significant bits)."""
+    a = np.abs(x)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return np.exp2(np.maximum(e, -126) - 7)
