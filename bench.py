@@ -1,0 +1,377 @@
+"""Benchmark of the paged-KV attention hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-prefill]
+
+One step is one pass of the hot path over the Llama-3-8B-shaped decode
+batch: kv_cache_write of the 256 new tokens (bf16), the split-K decode
+partition kernel and the merge kernel, with the 3.4 GB cache resident in HBM.
+The chunked-prefill kernel (16 sequences x 256 new tokens, window 4096) is
+timed in the same run and reported under "prefill".
+
+The line printed last is one JSON object: the step's algorithmic KV bytes per
+second ("value"), the decode partition kernel against the HBM roofline
+(timed with HIP events on the launch stream), and the fp64 oracle timed on the
+host ("cpu_baseline").
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attn: KV GB/s & % of HBM peak; prefill-chunk % MFMA peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+class Regions:
+    """roctx profiler regions: with `rocprofv3 --selected-regions` only the
+    timed loops (and the calibration copy) are profiled, not input generation.
+    Without a profiler attached the calls do nothing."""
+
+    def __init__(self):
+        import ctypes
+        self.lib = None
+        for name in ("librocprofiler-sdk-roctx.so.1", "librocprofiler-sdk-roctx.so"):
+            try:
+                self.lib = ctypes.CDLL(name)
+                break
+            except OSError:
+                continue
+
+    def resume(self):
+        if self.lib is not None:
+            self.lib.roctxProfilerResume(0)
+
+    def pause(self):
+        if self.lib is not None:
+            self.lib.roctxProfilerPause(0)
+
+
+REGIONS = None
+
+
+def kernel_source_hash(name: str) -> str:
+    p = os.path.join(ROOT, "paged_kv_cache_235_amd", "csrc", name)
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def read_traffic(tag: str, source: str):
+    """HBM bytes per launch measured with rocprofv3 counters, if they were taken
+    on the current kernel source (profiles/<tag>.traffic.txt)."""
+    path = os.path.join(PROFILES, f"{tag}.traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha256_16") != kernel_source_hash(source):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ------------------------------------------------------------------ decode step
+def decode_bytes(case):
+    """Algorithmic bytes of one decode call: K and V of every visible key once
+    per KV head (the GQA group shares the read), the block-table entries, Q
+    and the fp32 output."""
+    e = {"f32": 4, "bf16": 2, "i8": 1}[case.kv_dtype]
+    lens = case.seq_lens.astype(np.int64)
+    eff = np.minimum(lens, case.window) if case.window > 0 else lens
+    kv = int(eff.sum()) * case.num_kv_heads * case.head_dim * e * 2
+    if case.kv_dtype == "i8":
+        kv += int(eff.sum()) * case.num_kv_heads * 2 * 2
+    table = int((-(-lens // case.block_size)).sum()) * 4
+    q = case.num_seqs * case.num_q_heads * case.head_dim * (4 if case.in_dtype == "f32" else 2)
+    out = case.num_seqs * case.num_q_heads * case.head_dim * 4
+    return {"kv": kv, "table": table, "q": q, "out": out}
+
+
+def write_bytes(num_tokens, num_kv_heads, head_dim, esz=2):
+    # read K and V, write them into the pools, read the slot ids
+    return 2 * 2 * num_tokens * num_kv_heads * head_dim * esz + 4 * num_tokens
+
+
+def bench_decode(args, torch, pkv, workloads, tl):
+    dev = torch.device("cuda", 0)
+    case = workloads.llama_decode()
+    print(f"[bench] decode setup: {case.num_seqs} seqs, {int(case.seq_lens.sum())} tokens, "
+          f"{case.num_blocks} blocks", flush=True)
+    pools = tl.alloc_pools(case, dev)
+    tl.write_tokens(case, pools, dev, "all")      # the step rewrites its new tokens with the same values
+    bt, lens, _ = tl.tables(case, dev)
+    q = case.q(dev)
+    new_k = case.kv_at("k", case.new_tokens(), dev)
+    new_v = case.kv_at("v", case.new_tokens(), dev)
+    new_slots = torch.from_numpy(case.new_slots()).to(dev)
+    out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    ws_bytes = pkv.decode_workspace_size(case.num_seqs, case.num_q_heads, case.head_dim,
+                                         case.max_blocks_per_seq, case.block_size, case.partition_size)
+    workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    print(f"[bench] decode setup done; workspace {ws_bytes / 2**20:.1f} MiB", flush=True)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        pkv.kv_cache_write(new_k, new_v, new_slots, pools["k"], pools["v"])
+        if ev:
+            ev[1].record()
+            pkv.set_decode_split_event(ev[2])
+        pkv.paged_attention_decode(q, pools["k"], pools["v"], bt, lens, case.softmax_scale,
+                                   partition_size=case.partition_size, out=out, workspace=workspace)
+        if ev:
+            pkv.set_decode_split_event(None)
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    REGIONS.resume()
+    start.record()
+    for i in range(args.steps):
+        step(evs[i])
+    end.record()
+    torch.cuda.synchronize()
+    REGIONS.pause()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    t_write = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    t_part = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    t_merge = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    t_step = np.array([e[0].elapsed_time(e[3]) for e in evs])
+
+    # correctness of the timed configuration, on a sample of sequences
+    check = sorted({int(np.argmax(case.seq_lens)), int(np.argmin(case.seq_lens)), 7, 100, 200})
+    sub = case.subset(check)
+    from oracle.cases import build_cache, expected_outputs
+    ref = expected_outputs(sub, cache=build_cache(sub, device=dev))
+    err = tl.assert_close(out[check], ref, "bf16", "bench decode")
+
+    b = decode_bytes(case)
+    wb = write_bytes(case.num_seqs, case.num_kv_heads, case.head_dim)
+    step_bytes = sum(b.values()) + wb
+    part_bytes = b["kv"] + b["table"] + b["q"]
+    part_s = float(np.mean(t_part)) / 1e3
+    achieved = part_bytes / part_s / 1e9
+    return {
+        "case": case,
+        "pools": pools,
+        "ms_per_step": total_ms / args.steps,
+        "wall_ms_per_step": wall * 1e3 / args.steps,
+        "step_bytes": step_bytes,
+        "breakdown_us": {"kv_cache_write": float(np.mean(t_write)) * 1e3,
+                         "decode_partition": float(np.mean(t_part)) * 1e3,
+                         "decode_merge": float(np.mean(t_merge)) * 1e3,
+                         "step_median": float(np.median(t_step)) * 1e3,
+                         "step_p10": float(np.percentile(t_step, 10)) * 1e3,
+                         "step_p90": float(np.percentile(t_step, 90)) * 1e3},
+        "bytes": b,
+        "roofline": {"kernel": "decode_partition_kernel<bf16, D=128, G=4>", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": read_traffic("decode_llama3_8b_shaped", "decode.hip"),
+                     "algorithmic_bytes_per_launch": part_bytes},
+        "max_abs_err": float(err),
+    }
+
+
+def cpu_baseline(case, torch, dev):
+    """The fp64 oracle (single-threaded C) on the whole decode step: K/V come
+    from the seeded generator (run on the GPU, copied to the host), the
+    oracle writes its own host pool; only gather + attention are timed."""
+    import oracle
+    from oracle.cases import build_cache, to_numpy
+    cache = build_cache(case, device=dev)
+    q = to_numpy(case.q())
+    t0 = time.perf_counter()
+    oracle.decode(cache, q, case.in_dtype, case.seq_lens, case.block_tables, case.softmax_scale,
+                  case.window)
+    dt = time.perf_counter() - t0
+    kv = decode_bytes(case)
+    step_bytes = sum(kv.values()) + write_bytes(case.num_seqs, case.num_kv_heads, case.head_dim)
+    return {"value": round(step_bytes / dt / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"the whole decode step: all {case.num_seqs} sequences, "
+                      f"{int(case.seq_lens.sum())} context tokens, gather + two-pass fp64 attention "
+                      f"on one host thread"}
+
+
+# ------------------------------------------------------------------ prefill
+def prefill_flops(case):
+    """Algorithmic flops: 4 * D per visible (query row, key) pair per query head."""
+    total = 0
+    for s in range(case.num_seqs):
+        L, C = int(case.seq_lens[s]), int(case.new_lens[s])
+        p = np.arange(L - C, L, dtype=np.int64)
+        vis = p + 1 if case.window <= 0 else np.minimum(p + 1, case.window)
+        total += int(vis.sum())
+    return 4 * case.head_dim * case.num_q_heads * total
+
+
+def bench_prefill(args, torch, pkv, workloads, tl):
+    dev = torch.device("cuda", 0)
+    case = workloads.prefill_window()
+    pools = tl.alloc_pools(case, dev)
+    tl.write_tokens(case, pools, dev, "all")      # the chunk's own tokens are rewritten before each call
+    bt, lens, cu = tl.tables(case, dev)
+    q = case.q(dev)
+    new_k = case.kv_at("k", case.new_tokens(), dev)
+    new_v = case.kv_at("v", case.new_tokens(), dev)
+    new_slots = torch.from_numpy(case.new_slots()).to(dev)
+    out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+
+    def call():
+        pkv.paged_attention_prefill_chunk(q, cu, lens, pools["k"], pools["v"], bt, case.max_q_len,
+                                          case.softmax_scale, sliding_window=case.window, out=out)
+
+    pkv.kv_cache_write(new_k, new_v, new_slots, pools["k"], pools["v"])
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    REGIONS.resume()
+    for e in evs:
+        e[0].record()
+        call()
+        e[1].record()
+    torch.cuda.synchronize()
+    REGIONS.pause()
+    t = np.array([a.elapsed_time(b) for a, b in evs])
+    check = [0, int(np.argmax(case.seq_lens)), int(np.argmin(case.seq_lens))]
+    sub = case.subset(sorted(set(check)))
+    from oracle.cases import build_cache, expected_outputs
+    ref = expected_outputs(sub, cache=build_cache(sub, device=dev))
+    cu_np = case.cu_q_lens
+    rows = np.concatenate([np.arange(cu_np[s], cu_np[s + 1]) for s in sorted(set(check))])
+    err = tl.assert_close(out[torch.from_numpy(rows).to(dev)], ref, "bf16", "bench prefill")
+    fl = prefill_flops(case)
+    sec = float(np.mean(t)) / 1e3
+    tf = fl / sec / 1e12
+    return {"workload": "chunked prefill: 16 sequences x 256 new tokens on 1024..16384-token paged "
+                        "contexts, 32 q / 8 kv heads, head_dim 128, bf16, causal + window 4096",
+            "us_per_call": round(sec * 1e6, 2), "us_p10": round(float(np.percentile(t, 10)) * 1e3, 2),
+            "us_p90": round(float(np.percentile(t, 90)) * 1e3, 2),
+            "roofline": {"kernel": "prefill_chunk_kernel<D=128>", "bound": "mfma", "achieved": round(tf, 1),
+                         "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                         "traffic": read_traffic("prefill_window", "prefill.hip"),
+                         "algorithmic_flops_per_launch": fl},
+            "max_abs_err": float(err)}
+
+
+def calibrate_copy(torch):
+    """A plain elementwise copy of known size (negation, so the kernel is easy to
+    pick out by name), for scaling rocprofv3 byte counters: each launch reads
+    and writes exactly 1 GiB."""
+    dev = torch.device("cuda", 0)
+    n = 1 << 28                      # 1 GiB of fp32
+    a = torch.ones(n, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    REGIONS.resume()
+    for _ in range(3):
+        torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    REGIONS.pause()
+    print(f"[bench] calibration copy: 3 launches, each {n * 4} bytes read and {n * 4} written", flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a 1 GiB device copy (scale for rocprofv3 byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the paged-attention path here has no multi-GPU "
+              "mode (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    global REGIONS
+    REGIONS = Regions()
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import paged_kv_cache_235_amd as pkv
+    import workloads
+    import pkv_testlib as tl
+
+    pkv.load_library()
+    if args.calibrate_copy:
+        calibrate_copy(torch)
+    d = bench_decode(args, torch, pkv, workloads, tl)
+    print(f"[bench] decode: {d['ms_per_step'] * 1e3:.1f} us/step, partition "
+          f"{d['breakdown_us']['decode_partition']:.1f} us = {d['roofline']['achieved']:.0f} GB/s", flush=True)
+    case = d.pop("case")
+    d.pop("pools")
+    torch.cuda.empty_cache()
+    pre = None
+    if not args.no_prefill:
+        try:
+            pre = bench_prefill(args, torch, pkv, workloads, tl)
+            print(f"[bench] prefill: {pre['us_per_call']:.1f} us = {pre['roofline']['achieved']:.0f} TFLOP/s",
+                  flush=True)
+        except pkv.PagedKVError as e:
+            pre = {"error": str(e)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (fp64 oracle, one thread)...", flush=True)
+        cpu = cpu_baseline(case, torch, torch.device("cuda", 0))
+        print(f"[bench] cpu baseline: {cpu['seconds']} s", flush=True)
+    value = d["step_bytes"] / (d["ms_per_step"] / 1e3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(d["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; K/V/Q ~ N(0,1) by Irwin-Hall, clipped log-normal context lengths, "
+                "shuffled physical blocks)",
+        "config": {"workload": "Llama-3-8B-shaped decode step: kv_cache_write of 256 new tokens + split-K "
+                               "paged decode (512-token partitions) + merge",
+                   "batch": case.num_seqs, "q_heads": case.num_q_heads, "kv_heads": case.num_kv_heads,
+                   "head_dim": case.head_dim, "block_size": case.block_size, "kv_dtype": case.kv_dtype,
+                   "context_tokens": int(case.seq_lens.sum()), "context_len_min": int(case.seq_lens.min()),
+                   "context_len_max": int(case.seq_lens.max()), "num_blocks": case.num_blocks,
+                   "partition_size": case.partition_size},
+        "roofline": d["roofline"],
+        "cpu_baseline": cpu,
+        "breakdown_us": d["breakdown_us"],
+        "algorithmic_bytes": d["bytes"],
+        "max_abs_err_sampled": d["max_abs_err"],
+        "prefill": pre,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -22,9 +22,11 @@ def to_numpy(t: torch.Tensor) -> np.ndarray:
     return t.numpy()
 
 
-def build_cache(case, kv_dtype: str | None = None, include_new: bool = True) -> Cache:
+def build_cache(case, kv_dtype: str | None = None, include_new: bool = True, device="cpu") -> Cache:
     """Poisoned pool, then every context token (and the step's new tokens)
-    written through the reference cache write, sequence by sequence."""
+    written through the reference cache write, sequence by sequence.  The
+    inputs are generated on ``device`` (the generator is bit-identical on
+    CPU and GPU) and copied to the host; the oracle itself runs on the host."""
     cache = Cache(case.num_blocks, case.block_size, case.num_kv_heads, case.head_dim,
                   kv_dtype or case.kv_dtype)
     for s in range(case.num_seqs):
@@ -33,8 +35,8 @@ def build_cache(case, kv_dtype: str | None = None, include_new: bool = True) -> 
             p1 = int(case.seq_lens[s])
         if p1 <= p0:
             continue
-        k = to_numpy(case.kv("k", s, p0, p1))
-        v = to_numpy(case.kv("v", s, p0, p1))
+        k = to_numpy(case.kv("k", s, p0, p1, device))
+        v = to_numpy(case.kv("v", s, p0, p1, device))
         cache.write(k, v, case.in_dtype, case.slots(s, p0, p1))
     return cache
 

@@ -47,6 +47,17 @@ def alloc_pools(case, dev, kv_dtype=None):
 def write_tokens(case, pools, dev, which="all", batch_tokens=1 << 16):
     """Write tokens of every sequence through kv_cache_write.
     which: 'context' (before this step), 'new' (this step's) or 'all'."""
+    if which == "all" and case.contiguous_counters():
+        # one run of counters: generate and write in large slices
+        slots = case.all_slots()
+        total = slots.shape[0]
+        for t0 in range(0, total, batch_tokens * 4):
+            t1 = min(total, t0 + batch_tokens * 4)
+            k = case.kv_tokens("k", t0, t1, dev)
+            v = case.kv_tokens("v", t0, t1, dev)
+            pkv.kv_cache_write(k, v, torch.from_numpy(slots[t0:t1]).to(dev), pools["k"], pools["v"],
+                               pools["ks"], pools["vs"])
+        return
     ks, vs, ss, n = [], [], [], 0
 
     def flush():

@@ -46,7 +46,8 @@ TAG_LENS = 6
 TAG_PERM = 7
 TAG_MISC = 8
 
-_CHUNK = 1 << 24  # elements per generation sub-call (bounds temporaries)
+_CHUNK = 1 << 24  # elements per generation sub-call on the CPU (bounds temporaries)
+_CHUNK_GPU = 1 << 26
 
 
 # ---------------------------------------------------------------- hashing
@@ -82,9 +83,9 @@ def hash_u32(seed: int, tag: int, counter: torch.Tensor) -> torch.Tensor:
     return _fmix32(_fmix32(lo ^ key) ^ hi)
 
 
-def _normal_chunk(seed: int, tag: int, start: int, count: int, device) -> torch.Tensor:
-    idx = torch.arange(start, start + count, dtype=torch.int64, device=device) * 6
-    acc = torch.zeros(count, dtype=torch.int64, device=device)
+def _normal_of(seed: int, tag: int, counters: torch.Tensor) -> torch.Tensor:
+    idx = counters * 6
+    acc = torch.zeros(counters.shape, dtype=torch.int64, device=counters.device)
     for j in range(6):
         h = hash_u32(seed, tag, idx + j)
         acc += (h & 0xFFFF) + (h >> 16)
@@ -92,11 +93,16 @@ def _normal_chunk(seed: int, tag: int, start: int, count: int, device) -> torch.
     return (acc - 393210).to(torch.float32) * (1.0 / 65536.0)
 
 
+def _normal_chunk(seed: int, tag: int, start: int, count: int, device) -> torch.Tensor:
+    return _normal_of(seed, tag, torch.arange(start, start + count, dtype=torch.int64, device=device))
+
+
 def normal_f32(seed: int, tag: int, start: int, count: int, device="cpu") -> torch.Tensor:
     """Approximately N(0,1) fp32 values for element counters [start, start+count)."""
     out = torch.empty(count, dtype=torch.float32, device=device)
-    for c0 in range(0, count, _CHUNK):
-        n = min(_CHUNK, count - c0)
+    step = _CHUNK if torch.device(device).type == "cpu" else _CHUNK_GPU
+    for c0 in range(0, count, step):
+        n = min(step, count - c0)
         out[c0:c0 + n] = _normal_chunk(seed, tag, start + c0, n, device)
     return out
 
@@ -244,8 +250,60 @@ class PagedCase:
         x = normal_f32(self.seed, TAG_Q, r0 * hd, (r1 - r0) * hd, device)
         return self._convert(x).view(r1 - r0, self.num_q_heads, self.head_dim)
 
+    def contiguous_counters(self) -> bool:
+        """True when the sequences' tokens are one run of counters (a fresh case)."""
+        lens = self.seq_lens.astype(np.int64)
+        return bool(np.array_equal(self.tok_base, np.concatenate([[0], np.cumsum(lens)[:-1]])))
+
+    def all_slots(self) -> np.ndarray:
+        """Slots of every token of every sequence, in counter order."""
+        if self.num_seqs == 0:
+            return np.zeros(0, np.int32)
+        return np.concatenate([self.slots(s, 0, int(self.seq_lens[s])) for s in range(self.num_seqs)])
+
+    def kv_tokens(self, which: str, t0: int, t1: int, device="cpu") -> torch.Tensor:
+        """K or V of global tokens [t0, t1) of a case with contiguous counters
+        (token t of sequence s is tok_base[s] + p): [t1-t0][Hkv][D]."""
+        hd = self.num_kv_heads * self.head_dim
+        n = (t1 - t0) * hd
+        tag = TAG_K if which == "k" else TAG_V
+        x = normal_f32(self.seed, tag, t0 * hd, n, device)
+        if self.outliers > 0.0:
+            otag = TAG_K_OUTLIER if which == "k" else TAG_V_OUTLIER
+            m = bernoulli_mask(self.seed, otag, t0 * hd, n, self.outliers, device)
+            x = torch.where(m, x * 8.0, x)
+        return self._convert(x).view(t1 - t0, self.num_kv_heads, self.head_dim)
+
+    def kv_at(self, which: str, tokens, device="cpu") -> torch.Tensor:
+        """K or V of arbitrary global token counters (tok_base[s] + p): [n][Hkv][D]."""
+        hd = self.num_kv_heads * self.head_dim
+        t = torch.as_tensor(np.asarray(tokens, dtype=np.int64)).to(device)
+        counters = (t.view(-1, 1) * hd + torch.arange(hd, dtype=torch.int64, device=device)).view(-1)
+        tag = TAG_K if which == "k" else TAG_V
+        x = _normal_of(self.seed, tag, counters)
+        if self.outliers > 0.0:
+            otag = TAG_K_OUTLIER if which == "k" else TAG_V_OUTLIER
+            thresh = int(math.ceil(self.outliers * 2.0 ** 32))
+            x = torch.where(hash_u32(self.seed, otag, counters) < thresh, x * 8.0, x)
+        return self._convert(x).view(-1, self.num_kv_heads, self.head_dim)
+
+    def new_tokens(self) -> np.ndarray:
+        """Global token counters of this step's new tokens, in sequence order."""
+        if self.num_seqs == 0:
+            return np.zeros(0, np.int64)
+        return np.concatenate([self.tok_base[s] + np.arange(*self.new_range(s), dtype=np.int64)
+                               for s in range(self.num_seqs)])
+
+    def new_slots(self) -> np.ndarray:
+        if self.num_seqs == 0:
+            return np.zeros(0, np.int32)
+        return np.concatenate([self.slots(s, *self.new_range(s)) for s in range(self.num_seqs)])
+
     def q(self, device="cpu") -> torch.Tensor:
         """All query rows of this step, in sequence order: [total_q][Hq][D]."""
+        qb = self.q_base
+        if self.num_seqs and np.array_equal(qb, np.concatenate([[0], np.cumsum(self.new_lens.astype(np.int64))[:-1]])):
+            return self.q_rows(0, self.total_q, device)
         return torch.cat([self.q_seq(s, device) for s in range(self.num_seqs)]) if self.num_seqs \
             else self.q_rows(0, 0, device)
 
