@@ -1,6 +1,323 @@
-// prefill.hip -- chunked-prefill paged attention (bf16 MFMA).  Not built yet.
+// prefill.hip -- paged attention for a chunk of new query tokens per sequence
+// (chunked prefill) on bf16 MFMA.
+//
+// "PyTorch LLM Serving Engine", What is implemented: prefill runs in
+// configurable chunks that share the step with decode work; Loading: the
+// chunk's K/V are written to their cache slots first, then the chunk attends
+// over the block table with a stable online softmax.  "MicroGen", Key
+// Features: grouped-query heads, window-length limit.
+//
+// Many query rows make Q.K^T and P.V dense contractions, so they run on
+// 32x32x16 MFMA with fp32 accumulation: Q.K^T in bf16 (the inputs' own
+// type, exact), P.V in fp16.  The softmax weights P are rounded to fp16
+// (11 significant bits) rather than bf16 (8): with few visible keys a bf16
+// weight error of 2^-9 moves the output by up to ~2^-9 * max|v|.  V is
+// converted from bf16 to fp16 as it is staged; that is exact for
+// 2^-14 <= |v| <= 65504 (smaller values keep an absolute error below 2^-25;
+// larger ones are outside what this path supports).
+//  * A workgroup (4 waves) owns 128 rows of one (sequence, KV head): rows are
+//    (chunk token, query head of the group) pairs, so all G heads of a group
+//    share every K/V tile the workgroup stages.  Each wave owns 32 rows.
+//  * Keys come in tiles of 64 (four 16-token blocks gathered through the
+//    block table) staged in LDS: K row-major, V transposed.  Tiles wholly
+//    outside every row's causal/window range are never visited; masks are
+//    applied only on edge tiles, by selection.
+//  * Each wave computes S^T = K Q^T, so one lane's accumulators hold one
+//    query row's scores: the row max/sum are lane-local plus one exchange
+//    with lane^32.  K rows are staged with bits 2 and 3 of the key index
+//    swapped, which makes each lane's 8 consecutive accumulators 8
+//    consecutive keys: converted to bf16 they are directly the B operand of
+//    O^T += V^T P^T, and V^T is read with one 16-byte LDS load per operand.
+//  * Online softmax in fp32 with exp2 (scale * log2 e folded in).
+//  * Workgroups of one (sequence, KV head) are placed on the same XCD so the
+//    K/V tiles they all read stay in that XCD's L2.
 #include "pkv_internal.h"
+#include "pkv_device.h"
 
 namespace pkv {
-hipError_t launch_prefill(const PrefillLaunch&, hipStream_t) { return hipErrorNotSupported; }
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRows = 128;              // query rows per workgroup
+constexpr int kKeys = 64;               // keys per tile
+constexpr int kBlk = 16;
+constexpr int kVtStride = kKeys + 8;    // halfwords per V^T row (16-byte aligned, conflict-free)
+constexpr int kXcds = 8;
+
+struct PrefillArgs {
+    const uint16_t* q;
+    void* out;
+    const uint16_t* k_pool;
+    const uint16_t* v_pool;
+    const int32_t* block_tables;
+    const int32_t* seq_lens;
+    const int32_t* cu_q_lens;
+    int32_t num_seqs, num_q_heads, num_kv_heads, group, num_blocks, max_blocks;
+    int32_t m_tiles;          // row tiles per (sequence, KV head)
+    int32_t total;            // num_seqs * num_kv_heads * m_tiles
+    int32_t window;
+    float scale_log2;
+    int32_t out_bf16;
+};
+
+__device__ __forceinline__ int swap23(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4_t& v) { return __builtin_bit_cast(bf16x8_t, v); }
+__device__ __forceinline__ f16x8_t as_f16x8(const u32x4_t& v) { return __builtin_bit_cast(f16x8_t, v); }
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void prefill_chunk_kernel(PrefillArgs a) {
+    constexpr int KS = D + 8;                   // halfwords per K row in LDS
+    constexpr int DK = D / 16;                  // k-steps of Q.K^T
+    constexpr int NT = D / 32;                  // 32-wide d tiles of the output
+    __shared__ __attribute__((aligned(16))) uint16_t s_k[kKeys * KS];
+    __shared__ __attribute__((aligned(16))) uint16_t s_vt[D * kVtStride];   // V^T as fp16
+
+    // ---- work item: XCD-major so that one (sequence, head) stays on one XCD
+    const int per_xcd = (a.total + kXcds - 1) / kXcds;
+    const int w_idx = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+    if (w_idx >= a.total) return;
+    const int mt = w_idx % a.m_tiles;
+    const int g = (w_idx / a.m_tiles) % a.num_kv_heads;
+    const int s = w_idx / (a.m_tiles * a.num_kv_heads);
+    const int G = a.group;
+    const int q0 = a.cu_q_lens[s];
+    const int C = a.cu_q_lens[s + 1] - q0;
+    const int L = min(a.seq_lens[s], a.max_blocks * kBlk);
+    const int nrows = C * G;
+    const int r0 = mt * kRows;
+    if (r0 >= nrows || C <= 0 || C > L) return;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int h = lane >> 5;                    // lane half
+    const int base_pos = L - C;                 // position of chunk token 0
+    const int p_min = base_pos + r0 / G;
+    const int p_max = base_pos + (min(nrows, r0 + kRows) - 1) / G;
+
+    // ---- this lane's query row and its Q fragment (B operand of S^T = K Q^T)
+    const int row = r0 + wave * 32 + (lane & 31);
+    const bool row_ok = row < nrows;
+    const int tok = row_ok ? row / G : 0;
+    const int jh = row_ok ? row - tok * G : 0;
+    const int p_row = row_ok ? base_pos + tok : p_max;
+    bf16x8_t qf[DK];
+    {
+        const uint16_t* qp = a.q + ((int64_t)(q0 + tok) * a.num_q_heads + g * G + jh) * D + 8 * h;
+#pragma unroll
+        for (int ks = 0; ks < DK; ++ks) {
+            u32x4_t v = {0u, 0u, 0u, 0u};
+            if (row_ok) v = *reinterpret_cast<const u32x4_t*>(qp + 16 * ks);
+            qf[ks] = as_bf16x8(v);
+        }
+    }
+
+    f32x16_t o[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[nt][v] = 0.0f;
+    float m_run = -INFINITY;     // running max of scaled scores (log2 units)
+    float l_run = 0.0f;          // this lane's share of the row sum
+
+    const int k_lo = (a.window > 0) ? max(0, p_min - a.window + 1) : 0;
+    const int kt_first = (k_lo / kKeys) * kKeys;
+    const int last_blk = (L - 1) / kBlk;        // last logical block with keys
+    const int32_t* table = a.block_tables + (int64_t)s * a.max_blocks;
+    const int64_t head_stride = (int64_t)kBlk * D;          // elements per (block, head) tile
+    const int64_t blk_stride = (int64_t)a.num_kv_heads * head_stride;
+
+    for (int kt = kt_first; kt <= p_max; kt += kKeys) {
+        // ---- stage the tile: waves 0-1 copy K (rows swapped), waves 2-3 transpose V
+        int vmask = 0;                          // bit b: block b of the tile holds keys
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int lb = kt / kBlk + b;
+            if (lb <= last_blk) {
+                const int id = table[lb];
+                if (id >= 0 && id < a.num_blocks) vmask |= 1 << b;
+            }
+        }
+        __syncthreads();                        // previous tile's LDS reads are done
+        if (wave < 2) {
+            const int t = tid;                  // 0..127
+            constexpr int CH = D / 8;           // 16-byte chunks per key row
+            for (int c = t; c < kKeys * CH; c += 128) {
+                const int key = c / CH, dc = c - (c / CH) * CH;
+                const int b = key / kBlk;
+                u32x4_t v = {0u, 0u, 0u, 0u};
+                if (vmask & (1 << b)) {
+                    const int id = table[kt / kBlk + b];
+                    v = *reinterpret_cast<const u32x4_t*>(
+                        a.k_pool + id * blk_stride + g * head_stride + (key % kBlk) * D + dc * 8);
+                }
+                *reinterpret_cast<u32x4_t*>(&s_k[swap23(key) * KS + dc * 8]) = v;
+            }
+        } else {
+            const int t = tid - 128;            // 0..127
+            constexpr int TASKS = (kKeys / 8) * (D / 8);
+            for (int task = t; task < TASKS; task += 128) {
+                const int kg = task % 8;        // lanes 0..7 of a group: 8 key groups, one d chunk
+                const int dc = task / 8;
+                const int key0 = kg * 8;
+                const int b = key0 / kBlk;
+                uint32_t w[8][4];
+                if (vmask & (1 << b)) {
+                    const int id = table[kt / kBlk + b];
+                    const uint16_t* vp = a.v_pool + id * blk_stride + g * head_stride + (key0 % kBlk) * D + dc * 8;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        u32x4_t v = *reinterpret_cast<const u32x4_t*>(vp + i * D);
+                        const bool live = kt + key0 + i < L;      // unwritten tail slots may hold NaN
+                        w[i][0] = live ? v[0] : 0u; w[i][1] = live ? v[1] : 0u;
+                        w[i][2] = live ? v[2] : 0u; w[i][3] = live ? v[3] : 0u;
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) w[i][0] = w[i][1] = w[i][2] = w[i][3] = 0u;
+                }
+                // 8x8 transpose, bf16 -> fp16: out row e = element e of keys key0..key0+7
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int word = e >> 1;
+                    u32x4_t r;
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const uint32_t a0 = w[2 * m][word], a1 = w[2 * m + 1][word];
+                        r[m] = (e & 1) ? pack_f16x2(bf16hi(a0), bf16hi(a1)) : pack_f16x2(bf16lo(a0), bf16lo(a1));
+                    }
+                    *reinterpret_cast<u32x4_t*>(&s_vt[(dc * 8 + e) * kVtStride + key0]) = r;
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---- S^T = K Q^T for the wave's 32 rows: two 32-key halves
+        f32x16_t sacc[2];
+#pragma unroll
+        for (int T = 0; T < 2; ++T) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) sacc[T][v] = 0.0f;
+#pragma unroll
+            for (int ks = 0; ks < DK; ++ks) {
+                const u32x4_t kv = *reinterpret_cast<const u32x4_t*>(&s_k[(32 * T + (lane & 31)) * KS + 16 * ks + 8 * h]);
+                sacc[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), qf[ks], sacc[T], 0, 0, 0);
+            }
+        }
+
+        // ---- masks (edge tiles only): key of accumulator v = kt + 32T + 16(v/8) + 8h + v%8
+        const bool full = vmask == 15 && kt + kKeys - 1 <= p_min && (a.window <= 0 || kt >= p_max - a.window + 1);
+        if (!full) {
+#pragma unroll
+            for (int T = 0; T < 2; ++T)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int key = kt + 32 * T + 16 * (v / 8) + 8 * h + (v % 8);
+                    const bool vis = ((vmask >> ((key - kt) / kBlk)) & 1) && key <= p_row &&
+                                     (a.window <= 0 || key > p_row - a.window);
+                    sacc[T][v] = vis ? sacc[T][v] : -INFINITY;
+                }
+        }
+
+        // ---- online softmax for the row (lane-local + lane^32)
+        float mt_ = -INFINITY;
+#pragma unroll
+        for (int T = 0; T < 2; ++T)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) mt_ = fmaxf(mt_, sacc[T][v]);
+        mt_ = fmaxf(mt_, __shfl_xor(mt_, 32, kWave));
+        const float m_new = fmaxf(m_run, mt_ == -INFINITY ? -INFINITY : mt_ * a.scale_log2);
+        const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_run - m_new);
+        m_run = m_new;
+        const float msub = (m_new == -INFINITY) ? 0.0f : m_new;
+        uint32_t pw[2][8];                       // P^T as fp16 pairs: [T][4u + word]
+        float lsum = 0.0f;
+#pragma unroll
+        for (int T = 0; T < 2; ++T)
+#pragma unroll
+            for (int v = 0; v < 16; v += 2) {
+                const float x0 = sacc[T][v], x1 = sacc[T][v + 1];
+                const float p0 = (x0 == -INFINITY) ? 0.0f : fast_exp2(fmaf(x0, a.scale_log2, -msub));
+                const float p1 = (x1 == -INFINITY) ? 0.0f : fast_exp2(fmaf(x1, a.scale_log2, -msub));
+                lsum += p0 + p1;
+                pw[T][v / 2] = pack_f16x2(p0, p1);
+            }
+        l_run = l_run * alpha + lsum;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) o[nt][v] *= alpha;
+
+        // ---- O^T += V^T P^T: k-step ks covers keys 16ks..16ks+15 (tile T = ks/2, u = ks%2)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int T = ks >> 1, u = ks & 1;
+            u32x4_t pb;
+            pb[0] = pw[T][4 * u + 0]; pb[1] = pw[T][4 * u + 1];
+            pb[2] = pw[T][4 * u + 2]; pb[3] = pw[T][4 * u + 3];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const u32x4_t vv = *reinterpret_cast<const u32x4_t*>(&s_vt[(32 * nt + (lane & 31)) * kVtStride + 16 * ks + 8 * h]);
+                o[nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(vv), as_f16x8(pb), o[nt], 0, 0, 0);
+            }
+        }
+    }
+
+    // ---- normalise and store: lane holds d = 32nt + 8(v/4) + 4h + v%4 of its row
+    const float l_row = l_run + __shfl_xor(l_run, 32, kWave);
+    if (!row_ok) return;
+    const float inv = l_row > 0.0f ? 1.0f / l_row : 0.0f;
+    const int64_t obase = ((int64_t)(q0 + tok) * a.num_q_heads + g * G + jh) * D;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+            const int d = 32 * nt + 8 * v4 + 4 * h;
+            const float r0_ = o[nt][4 * v4 + 0] * inv, r1_ = o[nt][4 * v4 + 1] * inv;
+            const float r2_ = o[nt][4 * v4 + 2] * inv, r3_ = o[nt][4 * v4 + 3] * inv;
+            if (a.out_bf16) {
+                u32x2_t pk;
+                pk[0] = pack_bf16x2(r0_, r1_);
+                pk[1] = pack_bf16x2(r2_, r3_);
+                *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(a.out) + obase + d) = pk;
+            } else {
+                f32x4_t fv = {r0_, r1_, r2_, r3_};
+                *reinterpret_cast<f32x4_t*>(static_cast<float*>(a.out) + obase + d) = fv;
+            }
+        }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillLaunch& L, hipStream_t stream) {
+    PrefillArgs a;
+    a.q = static_cast<const uint16_t*>(L.q);
+    a.out = L.out;
+    a.k_pool = static_cast<const uint16_t*>(L.k_pool);
+    a.v_pool = static_cast<const uint16_t*>(L.v_pool);
+    a.block_tables = L.block_tables;
+    a.seq_lens = L.seq_lens;
+    a.cu_q_lens = L.cu_q_lens;
+    a.num_seqs = L.num_seqs;
+    a.num_q_heads = L.num_q_heads;
+    a.num_kv_heads = L.num_kv_heads;
+    a.group = L.num_q_heads / L.num_kv_heads;
+    a.num_blocks = L.num_blocks;
+    a.max_blocks = L.max_blocks_per_seq;
+    const int64_t rows = (int64_t)L.max_q_len * a.group;
+    a.m_tiles = (int32_t)((rows + kRows - 1) / kRows);
+    const int64_t total = (int64_t)L.num_seqs * L.num_kv_heads * a.m_tiles;
+    if (total > INT32_MAX / 2) return hipErrorInvalidValue;
+    a.total = (int32_t)total;
+    a.window = L.window;
+    a.scale_log2 = L.softmax_scale * kLog2e;
+    a.out_bf16 = L.out_bf16;
+    const int64_t grid = ((total + kXcds - 1) / kXcds) * kXcds;
+    if (L.head_dim == 64)
+        return launch(prefill_chunk_kernel<64>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+    return launch(prefill_chunk_kernel<128>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+}
+
 }  // namespace pkv

@@ -1,0 +1,107 @@
+"""GPU paged_attention_prefill_chunk against the fp64 oracle.
+
+Chunks of new tokens are written through kv_cache_write into a NaN-poisoned,
+block-shuffled pool, then attended with causal and sliding-window masks on
+bf16 MFMA; sizes span several 128-row and 64-key tiles with ragged tails."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from oracle.cases import build_cache, expected_outputs, to_numpy
+from pkv_testlib import alloc_pools, assert_close, bf16_ulp, device, run_prefill, write_tokens
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(seq_lens, new_lens, hq=8, hkv=2, d=128, window=0, seed=81):
+    return workloads.make_case("prefill", seed, seq_lens, new_lens, hq, hkv, d, window=window, kind="prefill")
+
+
+def _gpu(case, **kw):
+    dev = device()
+    pools = alloc_pools(case, dev)
+    write_tokens(case, pools, dev, "all")
+    out = run_prefill(case, pools, dev, **kw)
+    torch.cuda.synchronize()
+    return out, pools
+
+
+SHAPES = [  # seq_lens, new_lens
+    ([40, 17, 300], [40, 17, 300]),           # whole sequences from position 0
+    ([1, 2, 33, 64, 65], [1, 2, 30, 5, 65]),
+    ([1000, 700, 129], [256, 100, 33]),
+    ([2100, 64], [31, 64]),
+]
+
+
+@pytest.mark.parametrize("lens,new", SHAPES, ids=["from0", "small", "mid", "long"])
+@pytest.mark.parametrize("window", [0, 1, 17, 100, 512])
+def test_prefill_matches_oracle(lens, new, window):
+    case = _case(lens, new, window=window)
+    out, _ = _gpu(case)
+    assert_close(out, expected_outputs(case), "bf16", f"W={window}")
+
+
+GEOMS = [(4, 4, 128), (8, 2, 64), (12, 2, 128), (6, 1, 64), (32, 8, 128), (16, 2, 128), (5, 5, 64)]
+
+
+@pytest.mark.parametrize("hq,hkv,d", GEOMS, ids=[f"{g[0]}q{g[1]}kv-D{g[2]}" for g in GEOMS])
+def test_prefill_group_sizes_and_head_dims(hq, hkv, d):
+    case = _case([300, 77, 1500], [130, 77, 40], hq=hq, hkv=hkv, d=d, window=200)
+    out, _ = _gpu(case)
+    assert_close(out, expected_outputs(case), "bf16")
+
+
+def test_prefill_bf16_output():
+    case = _case([400, 90], [200, 90], window=128)
+    out, _ = _gpu(case, out_dtype=torch.bfloat16)
+    ref = expected_outputs(case)
+    got = out.float().cpu().double().numpy()
+    assert (np.abs(got - ref) <= bf16_ulp(ref) + 2e-3).all()
+
+
+def test_prefill_block_permutation_and_reruns_are_bit_identical():
+    case = _case([600, 250], [256, 250], window=300)
+    a, pools = _gpu(case)
+    b = run_prefill(case, pools, device())
+    c, _ = _gpu(case.subset(range(case.num_seqs)))
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    assert torch.equal(a, c)
+
+
+def test_prefill_single_row_chunks_match_decode_semantics():
+    case = _case([5, 300, 1029], [1, 1, 1], hq=8, hkv=2, window=0)
+    out, _ = _gpu(case)
+    assert_close(out, expected_outputs(case), "bf16")
+
+
+def test_prefill_window_4096_full_size_sampled_rows():
+    """16 sequences x 256 new tokens on 1024..16384-token contexts, window 4096,
+    32 q / 8 kv heads -- the benchmark's launch configuration.  Rows are
+    sampled (first/last of each 128-row tile edge) and checked against the
+    oracle's decode over the matching prefix (pinned equal to chunk rows)."""
+    case = workloads.prefill_window()
+    out, _ = _gpu(case)
+    assert torch.isfinite(out).all()
+    picks = [int(np.argmin(case.seq_lens)), int(np.argmax(case.seq_lens)), 3]
+    sub = case.subset(sorted(set(picks)))
+    cache = build_cache(sub, device=device())
+    q = to_numpy(sub.q(device()))
+    cu_full = case.cu_q_lens
+    for si, s in enumerate(sorted(set(picks))):
+        L, C = int(case.seq_lens[s]), int(case.new_lens[s])
+        for i in (0, 1, 31, 32, 63, 127, 128, 200, 255):
+            row = int(sub.cu_q_lens[si]) + i
+            ref = oracle.decode(cache, q[row:row + 1], "bf16", np.array([L - C + i + 1], np.int32),
+                                sub.block_tables[si:si + 1], sub.softmax_scale, sub.window)
+            assert_close(out[cu_full[s] + i:cu_full[s] + i + 1], ref, "bf16", f"seq {s} row {i}")
+
+
+def test_prefill_zero_scale_and_empty_chunks():
+    case = workloads.make_case("z", 82, [50, 20, 70], [0, 20, 5], 8, 2, 128, softmax_scale=0.0,
+                               window=10, kind="prefill")
+    out, _ = _gpu(case)
+    assert_close(out, expected_outputs(case), "bf16")
