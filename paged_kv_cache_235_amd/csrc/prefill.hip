@@ -42,7 +42,7 @@ constexpr int kThreads = 256;
 constexpr int kRows = 128;              // query rows per workgroup
 constexpr int kKeys = 64;               // keys per tile
 constexpr int kBlk = 16;
-constexpr int kVtStride = kKeys + 8;    // halfwords per V^T row (16-byte aligned, conflict-free)
+constexpr int kVtStride = kKeys + 8;    // halfwords per V^T row (16-byte aligned)
 constexpr int kXcds = 8;
 
 struct PrefillArgs {
@@ -66,11 +66,21 @@ __device__ __forceinline__ int swap23(int k) { return (k & ~12) | ((k & 4) << 1)
 __device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4_t& v) { return __builtin_bit_cast(bf16x8_t, v); }
 __device__ __forceinline__ f16x8_t as_f16x8(const u32x4_t& v) { return __builtin_bit_cast(f16x8_t, v); }
 
+// Vt (V transposed, fp16) row d (72 halfwords apart) holds 8 groups of 8
+// keys; group g sits at position g ^ ((d >> 4) & 7).  On gfx950's LDS (64
+// banks, a 16-byte access served 16 lanes per pass) this keeps both the
+// staging writes (rows 4q + e of 16 consecutive q) and the MFMA operand reads
+// (rows d..d+15 of one group) at one pass per 16 lanes.
+__device__ __forceinline__ int vt_col(int d, int g) { return ((g ^ ((d >> 4) & 7)) << 3); }
+
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void prefill_chunk_kernel(PrefillArgs a) {
     constexpr int KS = D + 8;                   // halfwords per K row in LDS
     constexpr int DK = D / 16;                  // k-steps of Q.K^T
     constexpr int NT = D / 32;                  // 32-wide d tiles of the output
+    constexpr int KCH = kKeys * (D / 8) / kThreads;   // 16-byte K chunks staged per thread
+    constexpr int VTASKS = 8 * (D / 4);         // (8-key group, 4 dims) pieces of V per tile
+    constexpr float kRescale = 8.0f;            // rescale O only when a row max grows by > 2^8
     __shared__ __attribute__((aligned(16))) uint16_t s_k[kKeys * KS];
     __shared__ __attribute__((aligned(16))) uint16_t s_vt[D * kVtStride];   // V^T as fp16
 
@@ -119,7 +129,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_chunk_kernel(PrefillArgs 
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int v = 0; v < 16; ++v) o[nt][v] = 0.0f;
-    float m_run = -INFINITY;     // running max of scaled scores (log2 units)
+    float m_used = -INFINITY;    // max the weights are taken against (log2 units)
     float l_run = 0.0f;          // this lane's share of the row sum
 
     const int k_lo = (a.window > 0) ? max(0, p_min - a.window + 1) : 0;
@@ -129,70 +139,95 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_chunk_kernel(PrefillArgs 
     const int64_t head_stride = (int64_t)kBlk * D;          // elements per (block, head) tile
     const int64_t blk_stride = (int64_t)a.num_kv_heads * head_stride;
 
-    for (int kt = kt_first; kt <= p_max; kt += kKeys) {
-        // ---- stage the tile: waves 0-1 copy K (rows swapped), waves 2-3 transpose V
-        int vmask = 0;                          // bit b: block b of the tile holds keys
+    // ---- staging roles (every thread): KCH 16-byte K chunks and one V piece
+    //  K chunk c = tid + 256 i: key c / (D/8), dims (c % (D/8)) * 8 .. +8
+    //  V piece t = tid: dims 4 * (t % (D/4)) .. +4 of keys 8 * (t / (D/4)) .. +8
+    const bool v_task = tid < VTASKS;
+    const int v_dq = tid % (D / 4);
+    const int v_kg = tid / (D / 4);
+    u32x4_t kreg[KCH];
+    u32x2_t vreg[8];
+    int ids[4];                                 // physical blocks of the tile (0 when invalid)
+    int vmask = 0;                              // bit b: block b of the tile holds keys
+
+    // The tile's block ids are wave-uniform: read once, before any K/V load,
+    // so the 12 loads of a tile issue back to back.
+    auto tile_ids = [&](int kt) {
+        int m = 0;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const int lb = kt / kBlk + b;
-            if (lb <= last_blk) {
-                const int id = table[lb];
-                if (id >= 0 && id < a.num_blocks) vmask |= 1 << b;
+            const int id = lb <= last_blk ? table[lb] : -1;
+            const bool ok = id >= 0 && id < a.num_blocks;
+            ids[b] = ok ? id : 0;               // an invalid block reads block 0 and is masked
+            m |= (ok ? 1 : 0) << b;
+        }
+        return m;
+    };
+    auto pick = [&](int b) {                    // ids[b] without dynamic register indexing
+        return b == 0 ? ids[0] : b == 1 ? ids[1] : b == 2 ? ids[2] : ids[3];
+    };
+    auto load_tile = [&]() {
+#pragma unroll
+        for (int i = 0; i < KCH; ++i) {
+            const int c = tid + kThreads * i;
+            const int key = c / (D / 8), dc = c % (D / 8);
+            kreg[i] = *reinterpret_cast<const u32x4_t*>(
+                a.k_pool + pick(key / kBlk) * blk_stride + g * head_stride + (key % kBlk) * D + dc * 8);
+        }
+        if (v_task) {
+            const uint16_t* vp = a.v_pool + pick((8 * v_kg) / kBlk) * blk_stride + g * head_stride +
+                                 ((8 * v_kg) % kBlk) * D + 4 * v_dq;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) vreg[i] = *reinterpret_cast<const u32x2_t*>(vp + i * D);
+        }
+    };
+    auto store_tile = [&](int kt, int m) {
+#pragma unroll
+        for (int i = 0; i < KCH; ++i) {
+            const int c = tid + kThreads * i;
+            const int key = c / (D / 8), dc = c % (D / 8);
+            *reinterpret_cast<u32x4_t*>(&s_k[swap23(key) * KS + dc * 8]) = kreg[i];
+        }
+        if (v_task) {
+            // zero keys of invalid blocks and unwritten tail slots (>= L): they may hold NaN
+            const bool blk_live = (m >> ((8 * v_kg) / kBlk)) & 1;
+            uint32_t w[8][2];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const bool live = blk_live && kt + 8 * v_kg + i < L;
+                w[i][0] = live ? vreg[i][0] : 0u;
+                w[i][1] = live ? vreg[i][1] : 0u;
+            }
+            // 8 keys x 4 dims -> 4 rows of 8 keys, bf16 -> fp16
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int word = e >> 1;
+                u32x4_t r;
+#pragma unroll
+                for (int mm = 0; mm < 4; ++mm) {
+                    const uint32_t a0 = w[2 * mm][word], a1 = w[2 * mm + 1][word];
+                    r[mm] = (e & 1) ? pack_f16x2(bf16hi(a0), bf16hi(a1)) : pack_f16x2(bf16lo(a0), bf16lo(a1));
+                }
+                const int d = 4 * v_dq + e;
+                *reinterpret_cast<u32x4_t*>(&s_vt[d * kVtStride + vt_col(d, v_kg)]) = r;
             }
         }
-        __syncthreads();                        // previous tile's LDS reads are done
-        if (wave < 2) {
-            const int t = tid;                  // 0..127
-            constexpr int CH = D / 8;           // 16-byte chunks per key row
-            for (int c = t; c < kKeys * CH; c += 128) {
-                const int key = c / CH, dc = c - (c / CH) * CH;
-                const int b = key / kBlk;
-                u32x4_t v = {0u, 0u, 0u, 0u};
-                if (vmask & (1 << b)) {
-                    const int id = table[kt / kBlk + b];
-                    v = *reinterpret_cast<const u32x4_t*>(
-                        a.k_pool + id * blk_stride + g * head_stride + (key % kBlk) * D + dc * 8);
-                }
-                *reinterpret_cast<u32x4_t*>(&s_k[swap23(key) * KS + dc * 8]) = v;
-            }
-        } else {
-            const int t = tid - 128;            // 0..127
-            constexpr int TASKS = (kKeys / 8) * (D / 8);
-            for (int task = t; task < TASKS; task += 128) {
-                const int kg = task % 8;        // lanes 0..7 of a group: 8 key groups, one d chunk
-                const int dc = task / 8;
-                const int key0 = kg * 8;
-                const int b = key0 / kBlk;
-                uint32_t w[8][4];
-                if (vmask & (1 << b)) {
-                    const int id = table[kt / kBlk + b];
-                    const uint16_t* vp = a.v_pool + id * blk_stride + g * head_stride + (key0 % kBlk) * D + dc * 8;
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        u32x4_t v = *reinterpret_cast<const u32x4_t*>(vp + i * D);
-                        const bool live = kt + key0 + i < L;      // unwritten tail slots may hold NaN
-                        w[i][0] = live ? v[0] : 0u; w[i][1] = live ? v[1] : 0u;
-                        w[i][2] = live ? v[2] : 0u; w[i][3] = live ? v[3] : 0u;
-                    }
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) w[i][0] = w[i][1] = w[i][2] = w[i][3] = 0u;
-                }
-                // 8x8 transpose, bf16 -> fp16: out row e = element e of keys key0..key0+7
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int word = e >> 1;
-                    u32x4_t r;
-#pragma unroll
-                    for (int m = 0; m < 4; ++m) {
-                        const uint32_t a0 = w[2 * m][word], a1 = w[2 * m + 1][word];
-                        r[m] = (e & 1) ? pack_f16x2(bf16hi(a0), bf16hi(a1)) : pack_f16x2(bf16lo(a0), bf16lo(a1));
-                    }
-                    *reinterpret_cast<u32x4_t*>(&s_vt[(dc * 8 + e) * kVtStride + key0]) = r;
-                }
-            }
-        }
+    };
+
+    if (kt_first <= p_max) {
+        vmask = tile_ids(kt_first);
+        load_tile();
+    }
+    for (int kt = kt_first; kt <= p_max; kt += kKeys) {
+        __syncthreads();                        // every wave is done with the previous tile
+        const int tmask = vmask;
+        store_tile(kt, tmask);
         __syncthreads();
+        if (kt + kKeys <= p_max) {              // prefetch the next tile while this one is used
+            vmask = tile_ids(kt + kKeys);
+            load_tile();
+        }
 
         // ---- S^T = K Q^T for the wave's 32 rows: two 32-key halves
         f32x16_t sacc[2];
@@ -208,30 +243,40 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_chunk_kernel(PrefillArgs 
         }
 
         // ---- masks (edge tiles only): key of accumulator v = kt + 32T + 16(v/8) + 8h + v%8
-        const bool full = vmask == 15 && kt + kKeys - 1 <= p_min && (a.window <= 0 || kt >= p_max - a.window + 1);
+        const bool full = tmask == 15 && kt + kKeys - 1 <= p_min && (a.window <= 0 || kt >= p_max - a.window + 1);
         if (!full) {
 #pragma unroll
             for (int T = 0; T < 2; ++T)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int key = kt + 32 * T + 16 * (v / 8) + 8 * h + (v % 8);
-                    const bool vis = ((vmask >> ((key - kt) / kBlk)) & 1) && key <= p_row &&
+                    const bool vis = ((tmask >> ((key - kt) / kBlk)) & 1) && key <= p_row &&
                                      (a.window <= 0 || key > p_row - a.window);
                     sacc[T][v] = vis ? sacc[T][v] : -INFINITY;
                 }
         }
 
-        // ---- online softmax for the row (lane-local + lane^32)
+        // ---- online softmax for the row (lane-local + lane^32), lazy rescale
         float mt_ = -INFINITY;
 #pragma unroll
         for (int T = 0; T < 2; ++T)
 #pragma unroll
             for (int v = 0; v < 16; ++v) mt_ = fmaxf(mt_, sacc[T][v]);
         mt_ = fmaxf(mt_, __shfl_xor(mt_, 32, kWave));
-        const float m_new = fmaxf(m_run, mt_ == -INFINITY ? -INFINITY : mt_ * a.scale_log2);
-        const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_run - m_new);
-        m_run = m_new;
-        const float msub = (m_new == -INFINITY) ? 0.0f : m_new;
+        const float m_tile = mt_ == -INFINITY ? -INFINITY : mt_ * a.scale_log2;
+        const bool grow = m_tile > m_used + kRescale || (m_used == -INFINITY && m_tile != -INFINITY);
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+            const float m_new = grow ? m_tile : m_used;
+            const float alpha = (m_used == -INFINITY) ? 0.0f : fast_exp2(m_used - m_new);
+            m_used = m_new;
+            l_run *= grow ? alpha : 1.0f;
+            const float f = grow ? alpha : 1.0f;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) o[nt][v] *= f;
+        }
+        const float msub = (m_used == -INFINITY) ? 0.0f : m_used;
         uint32_t pw[2][8];                       // P^T as fp16 pairs: [T][4u + word]
         float lsum = 0.0f;
 #pragma unroll
@@ -244,11 +289,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_chunk_kernel(PrefillArgs 
                 lsum += p0 + p1;
                 pw[T][v / 2] = pack_f16x2(p0, p1);
             }
-        l_run = l_run * alpha + lsum;
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) o[nt][v] *= alpha;
+        l_run += lsum;
 
         // ---- O^T += V^T P^T: k-step ks covers keys 16ks..16ks+15 (tile T = ks/2, u = ks%2)
 #pragma unroll
@@ -259,7 +300,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_chunk_kernel(PrefillArgs 
             pb[2] = pw[T][4 * u + 2]; pb[3] = pw[T][4 * u + 3];
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
-                const u32x4_t vv = *reinterpret_cast<const u32x4_t*>(&s_vt[(32 * nt + (lane & 31)) * kVtStride + 16 * ks + 8 * h]);
+                const int d = 32 * nt + (lane & 31);
+                const u32x4_t vv = *reinterpret_cast<const u32x4_t*>(&s_vt[d * kVtStride + vt_col(d, 2 * ks + h)]);
                 o[nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(vv), as_f16x8(pb), o[nt], 0, 0, 0);
             }
         }
