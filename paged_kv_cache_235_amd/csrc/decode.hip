@@ -134,6 +134,28 @@ __device__ __forceinline__ void widen(const Words<WORDS>& t, float* x) {
     }
 }
 
+// One (block, KV head) tile as this lane holds it: NLOAD 16- or 8-byte pieces
+// (rows i * RPL + lane / LPR), plus the rows' INT8 scales.
+template <int KV, int D, int GT>
+struct Tile {
+    Words<Cfg<KV, D, GT>::WORDS> w[Cfg<KV, D, GT>::NLOAD];
+    float sc[Cfg<KV, D, GT>::NLOAD];
+};
+
+template <int KV, int D, int GT>
+__device__ __forceinline__ void load_tile(Tile<KV, D, GT>& t, const char* pool, const uint16_t* scales,
+                                          int64_t tile, int lane) {
+    using C = Cfg<KV, D, GT>;
+    const char* p = pool + tile * C::TILE_BYTES;
+#pragma unroll
+    for (int i = 0; i < C::NLOAD; ++i) t.w[i] = load_words<C::WORDS>(p + (i * kWave + lane) * C::LW);
+    if constexpr (KV == KV_I8) {
+#pragma unroll
+        for (int i = 0; i < C::NLOAD; ++i)
+            t.sc[i] = (float)__builtin_bit_cast(_Float16, scales[tile * kBlk + i * C::RPL + lane / C::LPR]);
+    }
+}
+
 template <int KV, int D, int GT>
 __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a) {
     using C = Cfg<KV, D, GT>;
@@ -144,7 +166,8 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int wave = tid >> 6;
+    // wave-uniform in a scalar register, so per-wave loop bounds are scalar branches
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int B = a.num_seqs;
 
     // ---- prefix of partition counts (each thread owns up to 8 consecutive sequences)
@@ -183,38 +206,46 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
     const int row_lane = lane / C::LPR;          // row of this lane inside each load
     const int col = (lane % C::LPR) * C::EPL;    // first column of this lane
 
-    for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    // work item -> (sequence, partition, KV head, query-head chunk) and its key range
+    struct Item {
+        int s, nparts, k, t0, t1, g, h0, nh;
+    };
+    auto item_info = [&](int item) {
+        Item I;
         const int gp = item / HC;
         const int hc = item - gp * HC;
-        const int g = hc / a.head_chunks;
-        const int hchunk = hc - g * a.head_chunks;
+        I.g = hc / a.head_chunks;
+        const int hchunk = hc - I.g * a.head_chunks;
         int lo_s = 0, hi_s = B - 1;                 // largest s with s_prefix[s] <= gp
         while (lo_s < hi_s) {
             const int mid = (lo_s + hi_s + 1) >> 1;
             if (s_prefix[mid] <= gp) lo_s = mid; else hi_s = mid - 1;
         }
-        const int s = lo_s;
-        const int nparts = s_prefix[s + 1] - s_prefix[s];
-        const int L = seq_len(a, s);
+        I.s = lo_s;
+        I.nparts = s_prefix[I.s + 1] - s_prefix[I.s];
+        const int L = seq_len(a, I.s);
         const int lo = first_key(a, L);
         const int P = a.part_tokens;
-        const int k = (P > 0 ? lo / P : 0) + (gp - s_prefix[s]);
-        const int t0 = P > 0 ? max(lo, k * P) : lo;
-        const int t1 = P > 0 ? min(L, (k + 1) * P) : L;
-        const int h0 = g * a.group + hchunk * GT;   // first query head of this item
-        const int nh = min(GT, a.group - hchunk * GT);
+        I.k = (P > 0 ? lo / P : 0) + (gp - s_prefix[I.s]);
+        I.t0 = P > 0 ? max(lo, I.k * P) : lo;
+        I.t1 = P > 0 ? min(L, (I.k + 1) * P) : L;
+        I.h0 = I.g * a.group + hchunk * GT;         // first query head of the item
+        I.nh = min(GT, a.group - hchunk * GT);
+        return I;
+    };
 
-        // ---- query fragment: this lane's columns of each head
-        uint32_t qw[GT][C::WORDS];      // bf16 pairs (bf16 pools)
-        float qf[GT][C::EPL];           // fp32 (fp32 and INT8 pools)
-        float qsum[GT];
+    // query fragment: this lane's columns of each head
+    uint32_t qw[GT][C::WORDS];      // bf16 pairs (bf16 pools)
+    float qf[GT][C::EPL];           // fp32 (fp32 and INT8 pools)
+    float qsum[GT];
+    auto load_q = [&](const Item& I) {
 #pragma unroll
         for (int j = 0; j < GT; ++j) {
-            const int64_t qoff = ((int64_t)s * a.num_q_heads + h0 + j) * D + col;
+            const int64_t qoff = ((int64_t)I.s * a.num_q_heads + I.h0 + j) * D + col;
             qsum[j] = 0.0f;
             if constexpr (KV == KV_BF16) {
                 Words<4> t{};
-                if (j < nh) {
+                if (j < I.nh) {
                     const u32x4_t v = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.q) + qoff);
                     t.w[0] = v[0]; t.w[1] = v[1]; t.w[2] = v[2]; t.w[3] = v[3];
                 }
@@ -224,7 +255,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
 #pragma unroll
                 for (int e = 0; e < C::EPL; ++e) {
                     float x = 0.0f;
-                    if (j < nh)
+                    if (j < I.nh)
                         x = a.q_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(a.q)[qoff + e])
                                      : static_cast<const float*>(a.q)[qoff + e];
                     qf[j][e] = x;
@@ -232,6 +263,40 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
                 }
             }
         }
+    };
+
+    // block ids of one chunk: this wave takes blocks wave, wave + 4, ...; lane j
+    // reads the id of its j-th one (invalid ids read block 0 and are masked)
+    int lid = 0;
+    uint64_t okmask = 0;
+    auto chunk_ids = [&](const Item& I, int fb, int nbw) {
+        bool lok = false;
+        lid = 0;
+        if (lane < nbw) {
+            const int id = a.block_tables[(int64_t)I.s * a.max_blocks + fb + wave + kWaves * lane];
+            lok = id >= 0 && id < a.num_blocks;
+            lid = lok ? id : 0;
+        }
+        okmask = __builtin_amdgcn_ballot_w64(lok);
+    };
+    auto tile_of = [&](int i, int g) {
+        return (int64_t)__builtin_amdgcn_readlane(lid, i) * a.num_kv_heads + g;
+    };
+    auto chunk_end = [](int c0, int t1) { return min(t1, (c0 / kChunk + 1) * kChunk); };
+    auto blocks_of_wave = [&](int c0, int c1) {
+        const int nblk = (c1 - 1) / kBlk - c0 / kBlk + 1;
+        return wave < nblk ? (nblk - 1 - wave) / kWaves + 1 : 0;
+    };
+
+    Tile<KV, D, GT> cur, nxt;
+    bool pre = false;            // the next item's ids, Q and first K tile are already loaded
+    Item nextI = item_info(blockIdx.x < total ? blockIdx.x : 0);
+    for (int item = blockIdx.x; item < total; item += gridDim.x) {
+        const Item I = nextI;
+        const bool pre_now = pre;
+        pre = false;
+        const int s = I.s, g = I.g, h0 = I.h0, nh = I.nh, k = I.k, nparts = I.nparts;
+        if (!pre_now) load_q(I);
 
         float m_run[GT], l_run[GT], acc[GT][C::EPL], psum[GT];
 #pragma unroll
@@ -243,45 +308,45 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
             for (int e = 0; e < C::EPL; ++e) acc[j][e] = 0.0f;
         }
 
-        const int32_t* table = a.block_tables + (int64_t)s * a.max_blocks;
-        for (int c0 = t0; c0 < t1;) {
-            const int c1 = min(t1, (c0 / kChunk + 1) * kChunk);
+        for (int c0 = I.t0; c0 < I.t1;) {
+            const int c1 = chunk_end(c0, I.t1);
             const int fb = c0 / kBlk;
             const int nblk = (c1 - 1) / kBlk - fb + 1;
             const int tbase = fb * kBlk;          // token of LDS logit slot 0
+            const int nbw = blocks_of_wave(c0, c1);
+            if (!(pre_now && c0 == I.t0)) {
+                chunk_ids(I, fb, nbw);
+                if (nbw > 0) load_tile<KV, D, GT>(cur, a.k_pool, a.k_scale, tile_of(0, g), lane);
+            }
 
-            // ---- phase 1: K tiles -> logits
-            for (int b = wave; b < nblk; b += kWaves) {
-                int blk = table[fb + b];
-                const bool blk_ok = blk >= 0 && blk < a.num_blocks;
-                if (!blk_ok) blk = 0;
-                const int64_t tile = (int64_t)blk * a.num_kv_heads + g;
-                const char* kp = a.k_pool + tile * C::TILE_BYTES;
+            // ---- phase 1: K tiles -> logits, one tile of lookahead.  The last
+            // iteration is peeled so the lookahead load is unconditional and the
+            // wait for the current tile never covers the next one.
+            auto k_step = [&](const Tile<KV, D, GT>& t, int it) {
+                const int b = wave + kWaves * it;
+                const bool blk_ok = (okmask >> it) & 1;
                 float part[C::NV];
 #pragma unroll
                 for (int i = 0; i < C::NLOAD; ++i) {
-                    const Words<C::WORDS> t = load_words<C::WORDS>(kp + (i * kWave + lane) * C::LW);
-                    float ks = 1.0f;
-                    if constexpr (KV == KV_I8) ks = (float)__builtin_bit_cast(_Float16, a.k_scale[tile * kBlk + i * C::RPL + row_lane]);
                     if constexpr (KV == KV_BF16) {
 #pragma unroll
                         for (int j = 0; j < GT; ++j) {
                             float d = 0.0f;
 #pragma unroll
                             for (int w = 0; w < C::WORDS; ++w)
-                                d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, t.w[w]),
+                                d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, t.w[i].w[w]),
                                                                     __builtin_bit_cast(bf16x2_t, qw[j][w]), d, false);
                             part[i * GT + j] = d;
                         }
                     } else {
                         float x[C::EPL];
-                        widen<KV, C::WORDS>(t, x);
+                        widen<KV, C::WORDS>(t.w[i], x);
 #pragma unroll
                         for (int j = 0; j < GT; ++j) {
                             float d = 0.0f;
 #pragma unroll
                             for (int e = 0; e < C::EPL; ++e) d = fmaf(qf[j][e], x[e], d);
-                            if constexpr (KV == KV_I8) d = (d - 128.0f * qsum[j]) * ks;
+                            if constexpr (KV == KV_I8) d = (d - 128.0f * qsum[j]) * t.sc[i];
                             part[i * GT + j] = d;
                         }
                     }
@@ -299,7 +364,18 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
                         s_buf[slot * C::GTP + j] = ok ? part[kk] * a.scale_log2 : -INFINITY;
                     }
                 }
+            };
+            {
+                int it = 0;
+                for (; it + 1 < nbw; ++it) {
+                    load_tile<KV, D, GT>(nxt, a.k_pool, a.k_scale, tile_of(it + 1, g), lane);
+                    k_step(cur, it);
+                    cur = nxt;
+                }
+                if (it < nbw) k_step(cur, it);
             }
+            // the first V tile is in flight while the softmax runs
+            if (nbw > 0) load_tile<KV, D, GT>(cur, a.v_pool, a.v_scale, tile_of(0, g), lane);
             __syncthreads();
 
             // ---- softmax statistics of the chunk
@@ -352,23 +428,19 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
                 for (int e = 0; e < C::EPL; ++e) acc[j][e] *= alpha;
             }
 
-            // ---- phase 2: V tiles, p * v
-            for (int b = wave; b < nblk; b += kWaves) {
-                int blk = table[fb + b];
-                const bool blk_ok = blk >= 0 && blk < a.num_blocks;
-                if (!blk_ok) blk = 0;
-                const int64_t tile = (int64_t)blk * a.num_kv_heads + g;
-                const char* vp = a.v_pool + tile * C::TILE_BYTES;
+            // ---- phase 2: V tiles, p * v, one tile of lookahead (last iteration peeled)
+            auto v_step = [&](const Tile<KV, D, GT>& t, int it) {
+                const int b = wave + kWaves * it;
+                const bool blk_ok = (okmask >> it) & 1;
                 const bool full = blk_ok && tbase + b * kBlk >= c0 && tbase + (b + 1) * kBlk <= c1;
 #pragma unroll
                 for (int i = 0; i < C::NLOAD; ++i) {
-                    Words<C::WORDS> t = load_words<C::WORDS>(vp + (i * kWave + lane) * C::LW);
+                    Words<C::WORDS> wv = t.w[i];
                     const int slot = b * kBlk + i * C::RPL + row_lane;
+                    const bool row_ok = full || (blk_ok && tbase + slot >= c0 && tbase + slot < c1);
                     if (!full) {
-                        const int tok = tbase + slot;
-                        const bool ok = blk_ok && tok >= c0 && tok < c1;
 #pragma unroll
-                        for (int w = 0; w < C::WORDS; ++w) t.w[w] = ok ? t.w[w] : 0u;
+                        for (int w = 0; w < C::WORDS; ++w) wv.w[w] = row_ok ? wv.w[w] : 0u;
                     }
                     float p[C::GTP];
                     const f32x4_t p0 = *reinterpret_cast<const f32x4_t*>(&s_buf[slot * C::GTP]);
@@ -378,24 +450,46 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
                         p[4] = p1[0]; p[5] = p1[1]; p[6] = p1[2]; p[7] = p1[3];
                     }
                     if constexpr (KV == KV_I8) {
-                        const float vs = (float)__builtin_bit_cast(_Float16, a.v_scale[tile * kBlk + i * C::RPL + row_lane]);
 #pragma unroll
                         for (int j = 0; j < GT; ++j) {
-                            p[j] = (full || (blk_ok && tbase + slot >= c0 && tbase + slot < c1)) ? p[j] * vs : 0.0f;
+                            p[j] = row_ok ? p[j] * t.sc[i] : 0.0f;
                             psum[j] += p[j];
                         }
                     }
                     float x[C::EPL];
-                    widen<KV, C::WORDS>(t, x);
+                    widen<KV, C::WORDS>(wv, x);
 #pragma unroll
                     for (int j = 0; j < GT; ++j)
 #pragma unroll
                         for (int e = 0; e < C::EPL; ++e) acc[j][e] = fmaf(p[j], x[e], acc[j][e]);
                 }
+            };
+            {
+                int it = 0;
+                for (; it + 1 < nbw; ++it) {
+                    load_tile<KV, D, GT>(nxt, a.v_pool, a.v_scale, tile_of(it + 1, g), lane);
+                    v_step(cur, it);
+                    cur = nxt;
+                }
+                if (it < nbw) v_step(cur, it);
+            }
+            if (c1 >= I.t1 && item + (int)gridDim.x < total) {
+                // last chunk: start the next item's loads now (Q, block ids, first K tile);
+                // they complete while this item is combined and written
+                nextI = item_info(item + gridDim.x);
+                if (nextI.t0 < nextI.t1) {
+                    const int n0 = nextI.t0, n1 = chunk_end(n0, nextI.t1);
+                    const int nbw_n = blocks_of_wave(n0, n1);
+                    chunk_ids(nextI, n0 / kBlk, nbw_n);
+                    if (nbw_n > 0) load_tile<KV, D, GT>(cur, a.k_pool, a.k_scale, tile_of(0, nextI.g), lane);
+                }
+                load_q(nextI);
+                pre = true;
             }
             __syncthreads();
             c0 = c1;
         }
+        if (!pre && item + (int)gridDim.x < total) nextI = item_info(item + gridDim.x);
 
         // ---- combine the lanes of each column, then the waves
         if constexpr (KV == KV_I8) {
