@@ -372,10 +372,13 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
                     k_step(cur, it);
                     cur = nxt;
                 }
-                if (it < nbw) k_step(cur, it);
+                if (it < nbw) {
+                    // the first V tile streams in during the last K step and the softmax
+                    load_tile<KV, D, GT>(nxt, a.v_pool, a.v_scale, tile_of(0, g), lane);
+                    k_step(cur, it);
+                    cur = nxt;
+                }
             }
-            // the first V tile is in flight while the softmax runs
-            if (nbw > 0) load_tile<KV, D, GT>(cur, a.v_pool, a.v_scale, tile_of(0, g), lane);
             __syncthreads();
 
             // ---- softmax statistics of the chunk
@@ -545,8 +548,12 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
 
 // Merge the partitions of every (sequence, head) with more than one:
 // out = sum_k 2^(m_k - M) o_k / sum_k 2^(m_k - M) l_k, M = max_k m_k.
+// One wave per (sequence, head): lane k owns partition k's weight (64 at a
+// time), broadcast with readlane; the D-wide partial rows are read 8
+// partitions at a time so their loads overlap.
 template <int D>
 __global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecodeArgs a) {
+    constexpr int E = D / kWave;                 // output elements per lane
     const int lane = threadIdx.x & (kWave - 1);
     const int pair = blockIdx.x * kWaves + (threadIdx.x >> 6);
     if (pair >= a.num_seqs * a.num_q_heads) return;
@@ -555,24 +562,45 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecodeArgs a) {
     if (n <= 1) return;
     const int L = seq_len(a, s);
     const int k0 = first_key(a, L) / a.part_tokens;
-    const float* ml = a.part_ml + (int64_t)pair * a.max_parts * 2;
-    const float* po = a.part_o + (int64_t)pair * a.max_parts * D;
+    const float* ml = a.part_ml + ((int64_t)pair * a.max_parts + k0) * 2;
+    const float* po = a.part_o + ((int64_t)pair * a.max_parts + k0) * D + lane * E;
 
     float M = -INFINITY;
-    for (int k = lane; k < n; k += kWave) M = fmaxf(M, ml[(k0 + k) * 2]);
+    for (int k = lane; k < n; k += kWave) M = fmaxf(M, ml[2 * k]);
     M = group_max<kWave>(M);
     float den = 0.0f;
-    for (int k = lane; k < n; k += kWave) den += fast_exp2(ml[(k0 + k) * 2] - M) * ml[(k0 + k) * 2 + 1];
-    den = group_sum<kWave>(den);
-    constexpr int E = D / kWave;
     float o[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) o[e] = 0.0f;
-    for (int k = 0; k < n; ++k) {
-        const float w = fast_exp2(ml[(k0 + k) * 2] - M);
+    for (int kb = 0; kb < n; kb += kWave) {
+        const int k = kb + lane;
+        float w = 0.0f;
+        if (k < n) {
+            w = fast_exp2(ml[2 * k] - M);
+            den += w * ml[2 * k + 1];
+        }
+        const int cnt = min(kWave, n - kb);
+        int j = 0;
+        for (; j + 8 <= cnt; j += 8) {
+            float v[8][E];
 #pragma unroll
-        for (int e = 0; e < E; ++e) o[e] = fmaf(w, po[(int64_t)(k0 + k) * D + lane * E + e], o[e]);
+            for (int u = 0; u < 8; ++u)
+#pragma unroll
+                for (int e = 0; e < E; ++e) v[u][e] = po[(int64_t)(kb + j + u) * D + e];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j + u));
+#pragma unroll
+                for (int e = 0; e < E; ++e) o[e] = fmaf(wu, v[u][e], o[e]);
+            }
+        }
+        for (; j < cnt; ++j) {
+            const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j));
+#pragma unroll
+            for (int e = 0; e < E; ++e) o[e] = fmaf(wu, po[(int64_t)(kb + j) * D + e], o[e]);
+        }
     }
+    den = group_sum<kWave>(den);
     const float inv = den > 0.0f ? 1.0f / den : 0.0f;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
