@@ -159,10 +159,14 @@ __device__ __forceinline__ void load_tile(Tile<KV, D, GT>& t, const char* pool, 
 template <int KV, int D, int GT>
 __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a) {
     using C = Cfg<KV, D, GT>;
-    constexpr int BUF = (kChunk * C::GTP > kWaves * GT * D) ? kChunk * C::GTP : kWaves * GT * D;
+    constexpr int WKEYS = kChunk / kWaves;       // keys of one wave in one chunk
     __shared__ int s_prefix[kMaxSeqs + 1];
-    __shared__ __attribute__((aligned(16))) float s_buf[BUF];
-    __shared__ float s_red[kWaves][2][C::GTP];
+    // per-wave logits / probabilities of the current chunk: [key][GTP]
+    __shared__ __attribute__((aligned(16))) float s_logit[kWaves][WKEYS * C::GTP];
+    // per-wave partial outputs and (m, l) of an item, double-buffered by item parity
+    __shared__ __attribute__((aligned(16))) float s_comb[2][kWaves][GT * D];
+    __shared__ float s_ml[2][kWaves][2][C::GTP];
+    static_assert(kThreads <= 2 * kWaves * GT * D, "prefix scan scratch");
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -181,7 +185,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
             cnt[i] = (i < per && s < B) ? num_parts(a, s) : 0;
             sum += cnt[i];
         }
-        int* scan = reinterpret_cast<int*>(s_buf);
+        int* scan = reinterpret_cast<int*>(&s_comb[0][0][0]);
         scan[tid] = sum;
         __syncthreads();
         for (int off = 1; off < kThreads; off <<= 1) {
@@ -289,6 +293,8 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
     };
 
     Tile<KV, D, GT> cur, nxt;
+    float* lg = s_logit[wave];   // this wave's logits
+    int parity = 0;              // combine buffer of the current item
     bool pre = false;            // the next item's ids, Q and first K tile are already loaded
     Item nextI = item_info(blockIdx.x < total ? blockIdx.x : 0);
     for (int item = blockIdx.x; item < total; item += gridDim.x) {
@@ -298,6 +304,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
         const int s = I.s, g = I.g, h0 = I.h0, nh = I.nh, k = I.k, nparts = I.nparts;
         if (!pre_now) load_q(I);
 
+        // running softmax state of this wave's keys
         float m_run[GT], l_run[GT], acc[GT][C::EPL], psum[GT];
 #pragma unroll
         for (int j = 0; j < GT; ++j) {
@@ -311,17 +318,17 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
         for (int c0 = I.t0; c0 < I.t1;) {
             const int c1 = chunk_end(c0, I.t1);
             const int fb = c0 / kBlk;
-            const int nblk = (c1 - 1) / kBlk - fb + 1;
-            const int tbase = fb * kBlk;          // token of LDS logit slot 0
+            const int tbase = fb * kBlk;          // first token of the chunk's first block
             const int nbw = blocks_of_wave(c0, c1);
             if (!(pre_now && c0 == I.t0)) {
                 chunk_ids(I, fb, nbw);
                 if (nbw > 0) load_tile<KV, D, GT>(cur, a.k_pool, a.k_scale, tile_of(0, g), lane);
             }
 
-            // ---- phase 1: K tiles -> logits, one tile of lookahead.  The last
-            // iteration is peeled so the lookahead load is unconditional and the
-            // wait for the current tile never covers the next one.
+            // ---- phase 1: this wave's K tiles (blocks wave, wave + 4, ...) -> logits,
+            // one tile of lookahead.  The last iteration is peeled so the lookahead
+            // load is unconditional and the wait for the current tile never covers
+            // the next one.
             auto k_step = [&](const Tile<KV, D, GT>& t, int it) {
                 const int b = wave + kWaves * it;
                 const bool blk_ok = (okmask >> it) & 1;
@@ -358,10 +365,10 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
                     const int idx = base + kk;
                     if (kk < valid) {
                         const int i = idx / GT, j = idx - (idx / GT) * GT;
-                        const int slot = b * kBlk + i * C::RPL + row_lane;
-                        const int tok = tbase + slot;
+                        const int r = i * C::RPL + row_lane;
+                        const int tok = tbase + b * kBlk + r;
                         const bool ok = blk_ok && tok >= c0 && tok < c1;
-                        s_buf[slot * C::GTP + j] = ok ? part[kk] * a.scale_log2 : -INFINITY;
+                        lg[(it * kBlk + r) * C::GTP + j] = ok ? part[kk] * a.scale_log2 : -INFINITY;
                     }
                 }
             };
@@ -379,52 +386,37 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
                     cur = nxt;
                 }
             }
-            __syncthreads();
+            // LDS operations of one wave take effect in program order; this keeps
+            // the compiler from moving the reads below above the writes above.
+            asm volatile("" ::: "memory");
 
-            // ---- softmax statistics of the chunk
-            const int T = nblk * kBlk;
+            // ---- softmax statistics of this wave's keys of the chunk (no other wave involved)
+            const int T = nbw * kBlk;
             float mloc[GT];
 #pragma unroll
             for (int j = 0; j < GT; ++j) mloc[j] = -INFINITY;
-            for (int t = tid; t < T; t += kThreads)
+            for (int t = lane; t < T; t += kWave)
 #pragma unroll
-                for (int j = 0; j < GT; ++j) mloc[j] = fmaxf(mloc[j], s_buf[t * C::GTP + j]);
-#pragma unroll
-            for (int j = 0; j < GT; ++j) {
-                mloc[j] = group_max<kWave>(mloc[j]);
-                if (lane == 0) s_red[wave][0][j] = mloc[j];
-            }
-            __syncthreads();
+                for (int j = 0; j < GT; ++j) mloc[j] = fmaxf(mloc[j], lg[t * C::GTP + j]);
             float m_new[GT], lloc[GT];
 #pragma unroll
             for (int j = 0; j < GT; ++j) {
-                float m = m_run[j];
-#pragma unroll
-                for (int w = 0; w < kWaves; ++w) m = fmaxf(m, s_red[w][0][j]);
-                m_new[j] = m;
+                m_new[j] = fmaxf(m_run[j], group_max<kWave>(mloc[j]));
                 lloc[j] = 0.0f;
             }
-            for (int t = tid; t < T; t += kThreads)
+            for (int t = lane; t < T; t += kWave)
 #pragma unroll
                 for (int j = 0; j < GT; ++j) {
-                    const float x = s_buf[t * C::GTP + j];
+                    const float x = lg[t * C::GTP + j];
                     const float p = (x == -INFINITY) ? 0.0f : fast_exp2(x - m_new[j]);
-                    s_buf[t * C::GTP + j] = p;
+                    lg[t * C::GTP + j] = p;
                     lloc[j] += p;
                 }
+            asm volatile("" ::: "memory");
 #pragma unroll
             for (int j = 0; j < GT; ++j) {
-                lloc[j] = group_sum<kWave>(lloc[j]);
-                if (lane == 0) s_red[wave][1][j] = lloc[j];
-            }
-            __syncthreads();
-#pragma unroll
-            for (int j = 0; j < GT; ++j) {
-                float l = 0.0f;
-#pragma unroll
-                for (int w = 0; w < kWaves; ++w) l += s_red[w][1][j];
                 const float alpha = (m_run[j] == -INFINITY) ? 0.0f : fast_exp2(m_run[j] - m_new[j]);
-                l_run[j] = l_run[j] * alpha + l;
+                l_run[j] = l_run[j] * alpha + group_sum<kWave>(lloc[j]);
                 m_run[j] = m_new[j];
                 psum[j] *= alpha;
 #pragma unroll
@@ -439,17 +431,19 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
 #pragma unroll
                 for (int i = 0; i < C::NLOAD; ++i) {
                     Words<C::WORDS> wv = t.w[i];
-                    const int slot = b * kBlk + i * C::RPL + row_lane;
-                    const bool row_ok = full || (blk_ok && tbase + slot >= c0 && tbase + slot < c1);
+                    const int r = i * C::RPL + row_lane;
+                    const int tok = tbase + b * kBlk + r;
+                    const bool row_ok = full || (blk_ok && tok >= c0 && tok < c1);
                     if (!full) {
 #pragma unroll
                         for (int w = 0; w < C::WORDS; ++w) wv.w[w] = row_ok ? wv.w[w] : 0u;
                     }
+                    const float* pp = &lg[(it * kBlk + r) * C::GTP];
                     float p[C::GTP];
-                    const f32x4_t p0 = *reinterpret_cast<const f32x4_t*>(&s_buf[slot * C::GTP]);
+                    const f32x4_t p0 = *reinterpret_cast<const f32x4_t*>(pp);
                     p[0] = p0[0]; p[1] = p0[1]; p[2] = p0[2]; p[3] = p0[3];
                     if constexpr (C::GTP == 8) {
-                        const f32x4_t p1 = *reinterpret_cast<const f32x4_t*>(&s_buf[slot * C::GTP + 4]);
+                        const f32x4_t p1 = *reinterpret_cast<const f32x4_t*>(pp + 4);
                         p[4] = p1[0]; p[5] = p1[1]; p[6] = p1[2]; p[7] = p1[3];
                     }
                     if constexpr (KV == KV_I8) {
@@ -476,25 +470,27 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
                 }
                 if (it < nbw) v_step(cur, it);
             }
+            // the next chunk's logits overwrite this chunk's probabilities
+            asm volatile("" ::: "memory");
             if (c1 >= I.t1 && item + (int)gridDim.x < total) {
                 // last chunk: start the next item's loads now (Q, block ids, first K tile);
                 // they complete while this item is combined and written
                 nextI = item_info(item + gridDim.x);
+                load_q(nextI);
                 if (nextI.t0 < nextI.t1) {
                     const int n0 = nextI.t0, n1 = chunk_end(n0, nextI.t1);
                     const int nbw_n = blocks_of_wave(n0, n1);
                     chunk_ids(nextI, n0 / kBlk, nbw_n);
                     if (nbw_n > 0) load_tile<KV, D, GT>(cur, a.k_pool, a.k_scale, tile_of(0, nextI.g), lane);
                 }
-                load_q(nextI);
                 pre = true;
             }
-            __syncthreads();
             c0 = c1;
         }
         if (!pre && item + (int)gridDim.x < total) nextI = item_info(item + gridDim.x);
 
-        // ---- combine the lanes of each column, then the waves
+        // ---- combine: the lanes of each column, then the waves, each wave's
+        // state rescaled to the common maximum
         if constexpr (KV == KV_I8) {
 #pragma unroll
             for (int j = 0; j < GT; ++j)
@@ -510,26 +506,42 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
                 for (int off = C::LPR; off < kWave; off <<= 1) v += __shfl_xor(v, off, kWave);
                 acc[j][e] = v;
             }
+        float* cb = s_comb[parity][wave];
         if (lane < C::LPR) {
 #pragma unroll
             for (int j = 0; j < GT; ++j)
 #pragma unroll
-                for (int e = 0; e < C::EPL; ++e) s_buf[(wave * GT + j) * D + col + e] = acc[j][e];
+                for (int e = 0; e < C::EPL; ++e) cb[j * D + col + e] = acc[j][e];
         }
-        __syncthreads();
+        if (lane == 0) {
+#pragma unroll
+            for (int j = 0; j < GT; ++j) {
+                s_ml[parity][wave][0][j] = m_run[j];
+                s_ml[parity][wave][1][j] = l_run[j];
+            }
+        }
+        // One barrier per item: the buffers alternate, so a wave that runs ahead
+        // writes the other buffer, and it can only come back to this one after
+        // every wave has passed the next item's barrier, i.e. finished reading.
+        // The barrier waits for LDS only; the next item's loads stay in flight.
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         for (int idx = tid; idx < GT * D; idx += kThreads) {
             const int j = idx / D, d = idx - (idx / D) * D;
             if (j >= nh) continue;
-            float o = 0.0f;
+            float M = -INFINITY;
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) o += s_buf[(w * GT + j) * D + d];
+            for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_ml[parity][w][0][j]);
+            float o = 0.0f, l = 0.0f;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                const float mw = s_ml[parity][w][0][j];
+                const float f = (mw == -INFINITY) ? 0.0f : fast_exp2(mw - M);
+                o = fmaf(f, s_comb[parity][w][j * D + d], o);
+                l = fmaf(f, s_ml[parity][w][1][j], l);
+            }
             const int h = h0 + j;
-            float mj = 0.0f, lj = 0.0f;
-#pragma unroll
-            for (int jj = 0; jj < GT; ++jj)
-                if (jj == j) { mj = m_run[jj]; lj = l_run[jj]; }
             if (nparts == 1) {
-                const float r = lj > 0.0f ? o / lj : 0.0f;
+                const float r = l > 0.0f ? o / l : 0.0f;
                 const int64_t oi = ((int64_t)s * a.num_q_heads + h) * D + d;
                 if (a.out_bf16) static_cast<uint16_t*>(a.out)[oi] = f32_to_bf16(r);
                 else static_cast<float*>(a.out)[oi] = r;
@@ -537,12 +549,12 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
                 const int64_t pi = ((int64_t)s * a.num_q_heads + h) * a.max_parts + k;
                 a.part_o[pi * D + d] = o;
                 if (d == 0) {
-                    a.part_ml[pi * 2] = mj;
-                    a.part_ml[pi * 2 + 1] = lj;
+                    a.part_ml[pi * 2] = M;
+                    a.part_ml[pi * 2 + 1] = l;
                 }
             }
         }
-        __syncthreads();
+        parity ^= 1;
     }
 }
 
