@@ -9,18 +9,21 @@
 //  * A work item is (sequence, partition of the context, KV head, chunk of at
 //    most 8 of its query heads).  The kernel is persistent: each workgroup
 //    first turns the context lengths into a prefix of per-sequence partition
-//    counts in LDS, then strides over the items.  No host knowledge of the
-//    lengths is needed and no empty workgroup is launched.
-//  * Inside an item the keys are taken in chunks of up to 512 tokens aligned
-//    to 512.  Phase 1: each of the 4 waves streams whole (block, KV head)
-//    K tiles -- one contiguous run, read with coalesced 16-byte loads -- and
-//    forms all the query heads' dot products from the same registers (one K
-//    read serves the whole group).  The per-lane partial sums are reduced
-//    with a transposed DPP butterfly and the scaled logits land in LDS.
-//    Softmax: the workgroup takes the chunk's maximum and exponentiates each
-//    logit once (exp2, scale * log2 e folded in).  Phase 2: the waves stream
-//    the V tiles of the same blocks and accumulate p * v.  Chunks are merged
-//    with the running-maximum rescale, so every K/V byte is read once.
+//    counts in LDS; items 0 .. grid-1 go to the workgroups in order, later ones
+//    are claimed from a counter in the workspace (balanced, and the items in
+//    flight stay neighbours).  No host knowledge of the lengths is needed.
+//  * Inside an item the 4 waves take the blocks round-robin.  Each wave streams
+//    its blocks' K and V tiles -- whole (block, KV head) runs, read with
+//    coalesced 16-byte loads -- as one sequence K0 V0 K1 V1 ..., each tile
+//    buffer reloaded as soon as its step is done, and the stream runs on
+//    across items, so the memory pipe never drains.  A K step forms all the
+//    query heads' dot products from the same registers (one K read serves the
+//    whole group), reduces the per-lane partial sums with a transposed DPP
+//    butterfly and updates an online softmax: the running maximum only moves
+//    (with a rescale of what was accumulated) when a logit passes it by more
+//    than 2^8, which after the first tile is rare.  The probabilities go
+//    through LDS to the V step, which accumulates p * v.  At the end of the
+//    item the 4 waves' (m, l, acc) are combined through LDS.
 //  * Keys outside the sequence, its window or a valid block are removed by
 //    selection (logit -inf, V row zeroed), never by multiplying by zero, so
 //    poisoned (NaN) tail slots cannot leak.
@@ -33,16 +36,19 @@ namespace pkv {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kChunk = 512;            // keys per softmax chunk
+constexpr int kBatchKeys = 64 * 4 * 16; // keys per batch of block ids (64 blocks per wave)
+constexpr float kRescale = 8.0f;       // lazy rescale threshold (log2 units)
 constexpr int kBlk = 16;               // tokens per cache block
 constexpr int kMaxSeqs = 2048;         // sequences per launch (LDS prefix)
 constexpr int kMaxGroup = 8;           // query heads per item
+constexpr size_t kTicketBytes = 256;   // workspace head: the item counter
 
 struct DecodeArgs {
     const void* q;
     void* out;
     float* part_ml;          // [num_seqs][Hq][max_parts][2]  running max (log2 units), sum
     float* part_o;           // [num_seqs][Hq][max_parts][D]  unnormalised outputs
+    unsigned* ticket;        // item counter (zero at launch), or null: items by stride
     const char* k_pool;
     const char* v_pool;
     const uint16_t* k_scale;
@@ -156,16 +162,26 @@ __device__ __forceinline__ void load_tile(Tile<KV, D, GT>& t, const char* pool, 
     }
 }
 
+// Values per lane left by tbfly<N, BIT>, and the lane bits across which the
+// lanes hold copies of the same quantity (the steps that had one value left).
+constexpr int tb_count(int n, int bit) { return bit == 0 ? n : (n >= 2 ? tb_count((n + 1) / 2, bit / 2) : 1); }
+constexpr int tb_dup(int n, int bit) {
+    return bit == 0 ? 0 : (n >= 2 ? tb_dup((n + 1) / 2, bit / 2) : (bit | tb_dup(1, bit / 2)));
+}
+
 template <int KV, int D, int GT>
 __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a) {
     using C = Cfg<KV, D, GT>;
-    constexpr int WKEYS = kChunk / kWaves;       // keys of one wave in one chunk
+    constexpr int NT = tb_count(C::NV, C::LPR / 2);   // logits per lane after the butterfly
+    constexpr int DUP = tb_dup(C::NV, C::LPR / 2);
     __shared__ int s_prefix[kMaxSeqs + 1];
-    // per-wave logits / probabilities of the current chunk: [key][GTP]
-    __shared__ __attribute__((aligned(16))) float s_logit[kWaves][WKEYS * C::GTP];
+    __shared__ int s_len[kMaxSeqs];              // visible context length of each sequence
+    // per-wave probabilities of the tile in hand: [key][GTP]
+    __shared__ __attribute__((aligned(16))) float s_p[kWaves][kBlk * C::GTP];
     // per-wave partial outputs and (m, l) of an item, double-buffered by item parity
     __shared__ __attribute__((aligned(16))) float s_comb[2][kWaves][GT * D];
     __shared__ float s_ml[2][kWaves][2][C::GTP];
+    __shared__ int s_next[2];                    // next items, by item parity
     static_assert(kThreads <= 2 * kWaves * GT * D, "prefix scan scratch");
 
     const int tid = threadIdx.x;
@@ -198,7 +214,10 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int s = tid * per + i;
-            if (i < per && s < B) s_prefix[s] = run;
+            if (i < per && s < B) {
+                s_prefix[s] = run;
+                s_len[s] = seq_len(a, s);
+            }
             run += cnt[i];
         }
         if (tid == kThreads - 1) s_prefix[B] = scan[tid];
@@ -220,17 +239,20 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
         const int hc = item - gp * HC;
         I.g = hc / a.head_chunks;
         const int hchunk = hc - I.g * a.head_chunks;
+        // LDS values are the same in every lane: keep them in scalar registers
+        auto uni = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
         int lo_s = 0, hi_s = B - 1;                 // largest s with s_prefix[s] <= gp
         while (lo_s < hi_s) {
             const int mid = (lo_s + hi_s + 1) >> 1;
-            if (s_prefix[mid] <= gp) lo_s = mid; else hi_s = mid - 1;
+            if (uni(s_prefix[mid]) <= gp) lo_s = mid; else hi_s = mid - 1;
         }
         I.s = lo_s;
-        I.nparts = s_prefix[I.s + 1] - s_prefix[I.s];
-        const int L = seq_len(a, I.s);
+        const int ps = uni(s_prefix[I.s]);
+        I.nparts = uni(s_prefix[I.s + 1]) - ps;
+        const int L = uni(s_len[I.s]);
         const int lo = first_key(a, L);
         const int P = a.part_tokens;
-        I.k = (P > 0 ? lo / P : 0) + (gp - s_prefix[I.s]);
+        I.k = (P > 0 ? lo / P : 0) + (gp - ps);
         I.t0 = P > 0 ? max(lo, I.k * P) : lo;
         I.t1 = P > 0 ? min(L, (I.k + 1) * P) : L;
         I.h0 = I.g * a.group + hchunk * GT;         // first query head of the item
@@ -269,66 +291,116 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
         }
     };
 
-    // block ids of one chunk: this wave takes blocks wave, wave + 4, ...; lane j
-    // reads the id of its j-th one (invalid ids read block 0 and are masked)
+    // Block ids of a batch of up to 64 blocks per wave: this wave takes blocks
+    // wave, wave + 4, ...; lane j holds the id of its j-th one.  ids_of issues
+    // the load (the id, or -1 for lanes past the wave's blocks); install makes
+    // them current, invalid ids reading block 0 under a cleared mask bit.
     int lid = 0;
     uint64_t okmask = 0;
-    auto chunk_ids = [&](const Item& I, int fb, int nbw) {
-        bool lok = false;
-        lid = 0;
-        if (lane < nbw) {
-            const int id = a.block_tables[(int64_t)I.s * a.max_blocks + fb + wave + kWaves * lane];
-            lok = id >= 0 && id < a.num_blocks;
-            lid = lok ? id : 0;
-        }
-        okmask = __builtin_amdgcn_ballot_w64(lok);
+    auto ids_of = [&](const Item& I, int c0, int nbw) {
+        int id = -1;
+        if (lane < nbw) id = a.block_tables[(int64_t)I.s * a.max_blocks + c0 / kBlk + wave + kWaves * lane];
+        return id;
+    };
+    auto valid_id = [&](int id) { return id >= 0 && id < a.num_blocks; };
+    auto install = [&](int id) {
+        const bool ok = valid_id(id);
+        lid = ok ? id : 0;
+        okmask = __builtin_amdgcn_ballot_w64(ok);
     };
     auto tile_of = [&](int i, int g) {
         return (int64_t)__builtin_amdgcn_readlane(lid, i) * a.num_kv_heads + g;
     };
-    auto chunk_end = [](int c0, int t1) { return min(t1, (c0 / kChunk + 1) * kChunk); };
+    auto batch_end = [](int c0, int t1) { return min(t1, (c0 / kBatchKeys + 1) * kBatchKeys); };
     auto blocks_of_wave = [&](int c0, int c1) {
+        if (c1 <= c0) return 0;
         const int nblk = (c1 - 1) / kBlk - c0 / kBlk + 1;
         return wave < nblk ? (nblk - 1 - wave) / kWaves + 1 : 0;
     };
 
-    Tile<KV, D, GT> cur, nxt;
-    float* lg = s_logit[wave];   // this wave's logits
-    int parity = 0;              // combine buffer of the current item
-    bool pre = false;            // the next item's ids, Q and first K tile are already loaded
-    Item nextI = item_info(blockIdx.x < total ? blockIdx.x : 0);
-    for (int item = blockIdx.x; item < total; item += gridDim.x) {
-        const Item I = nextI;
-        const bool pre_now = pre;
-        pre = false;
-        const int s = I.s, g = I.g, h0 = I.h0, nh = I.nh, k = I.k, nparts = I.nparts;
-        if (!pre_now) load_q(I);
+    // Items 0 .. grid-1 go to the workgroups in order; after that each workgroup
+    // takes the next unclaimed item from the counter, so the work stays balanced
+    // and the items in flight at any time are neighbours (adjacent KV heads of
+    // the same blocks).  The item after the current one is known an item ahead
+    // (s_next), so its loads can start before the current item is combined.
+    const bool dyn = a.ticket != nullptr;
+    if (dyn) {
+        if (tid == 0) s_next[1] = blockIdx.x < total ? (int)gridDim.x + (int)atomicAdd(a.ticket, 1u) : total;
+        __syncthreads();
+    }
 
-        // running softmax state of this wave's keys
-        float m_run[GT], l_run[GT], acc[GT][C::EPL], psum[GT];
+    // The wave's tiles form one stream K0 V0 K1 V1 ... across blocks, batches
+    // and items.  tk holds K tiles and tv V tiles; each is reloaded with the
+    // next tile of its kind as soon as its step is done (sched_barrier keeps the
+    // compiler from sinking the load), so one to two tiles are always in flight
+    // and there is no softmax phase to stall the stream: the softmax is online.
+    Tile<KV, D, GT> tk, tv;
+    float* lp = s_p[wave];
+    int parity = 0;              // combine buffer of the current item
+    Item I = item_info(blockIdx.x < total ? blockIdx.x : 0);
+    if ((int)blockIdx.x < total) {
+        load_q(I);
+        const int nbw0 = blocks_of_wave(I.t0, batch_end(I.t0, I.t1));
+        install(ids_of(I, I.t0, nbw0));
+        if (nbw0 > 0) {
+            load_tile<KV, D, GT>(tk, a.k_pool, a.k_scale, tile_of(0, I.g), lane);
+            load_tile<KV, D, GT>(tv, a.v_pool, a.v_scale, tile_of(0, I.g), lane);
+        }
+    }
+    // this lane's logits after the butterfly: quantity base + kk is head
+    // (base + kk) % GT of key row ((base + kk) / GT) * RPL + row_lane
+    int tb_base = 0, tb_valid = C::NV;
+    {
+        float dummy[C::NV];
+#pragma unroll
+        for (int v = 0; v < C::NV; ++v) dummy[v] = 0.0f;
+        tbfly<C::NV, C::LPR / 2>(dummy, lane, tb_base, tb_valid);
+    }
+    const bool owner = (lane & DUP) == 0;        // one lane per distinct quantity
+
+    for (int item = blockIdx.x, following; item < total; item = following) {
+        following = dyn ? __builtin_amdgcn_readfirstlane(s_next[parity ^ 1]) : item + (int)gridDim.x;
+        int claimed = 0;
+        if (dyn && wave == 0 && lane == 0 && following < total) claimed = (int)atomicAdd(a.ticket, 1u);
+        const bool have_next = following < total;
+        const Item NI = item_info(have_next ? following : item);
+        const int s = I.s, g = I.g, h0 = I.h0, nh = I.nh, k = I.k, nparts = I.nparts;
+
+        // running softmax state of this wave's keys: m per head (uniform), the
+        // same m per logit slot of this lane, l per logit slot, acc per column
+        float m_run[GT], m_lane[NT], l_lane[NT], acc[GT][C::EPL], psum[GT];
 #pragma unroll
         for (int j = 0; j < GT; ++j) {
             m_run[j] = -INFINITY;
-            l_run[j] = 0.0f;
             psum[j] = 0.0f;
 #pragma unroll
             for (int e = 0; e < C::EPL; ++e) acc[j][e] = 0.0f;
         }
+#pragma unroll
+        for (int kk = 0; kk < NT; ++kk) {
+            m_lane[kk] = -INFINITY;
+            l_lane[kk] = 0.0f;
+        }
 
-        for (int c0 = I.t0; c0 < I.t1;) {
-            const int c1 = chunk_end(c0, I.t1);
-            const int fb = c0 / kBlk;
-            const int tbase = fb * kBlk;          // first token of the chunk's first block
+        // one pass per batch of block ids; an empty item still makes one pass,
+        // which hands the stream over to the next item
+        int c0 = I.t0;
+        do {
+            const int c1 = batch_end(c0, I.t1);
+            const int tbase = (c0 / kBlk) * kBlk;   // first token of the batch's first block
             const int nbw = blocks_of_wave(c0, c1);
-            if (!(pre_now && c0 == I.t0)) {
-                chunk_ids(I, fb, nbw);
-                if (nbw > 0) load_tile<KV, D, GT>(cur, a.k_pool, a.k_scale, tile_of(0, g), lane);
-            }
+            // the batch after this one: the next of this item, else the first of the next item
+            const bool more = c1 < I.t1;
+            const bool any_next = more || have_next;
+            const Item& J = more ? I : NI;
+            const int jc0 = more ? c1 : NI.t0;
+            const int nbw_n = any_next ? blocks_of_wave(jc0, batch_end(jc0, J.t1)) : 0;
+            const int id_n = ids_of(J, jc0, nbw_n);
+            const int g_n = J.g;
 
-            // ---- phase 1: this wave's K tiles (blocks wave, wave + 4, ...) -> logits,
-            // one tile of lookahead.  The last iteration is peeled so the lookahead
-            // load is unconditional and the wait for the current tile never covers
-            // the next one.
+            // ---- K tile -> logits of its 16 keys for every head, online softmax
+            // update (rescale only when a logit passes the running maximum by
+            // more than 2^kRescale), probabilities to LDS
             auto k_step = [&](const Tile<KV, D, GT>& t, int it) {
                 const int b = wave + kWaves * it;
                 const bool blk_ok = (okmask >> it) & 1;
@@ -359,71 +431,55 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
                     }
                 }
                 int base = 0, valid = C::NV;
-                const int n = tbfly<C::NV, C::LPR / 2>(part, lane, base, valid);
+                tbfly<C::NV, C::LPR / 2>(part, lane, base, valid);
+                float x[NT];
+                bool over = false;
 #pragma unroll
-                for (int kk = 0; kk < n; ++kk) {
+                for (int kk = 0; kk < NT; ++kk) {
                     const int idx = base + kk;
+                    const int r = (idx / GT) * C::RPL + row_lane;
+                    const int tok = tbase + b * kBlk + r;
+                    const bool ok = kk < valid && blk_ok && tok >= c0 && tok < c1;
+                    x[kk] = ok ? part[kk] * a.scale_log2 : -INFINITY;
+                    over |= x[kk] > m_lane[kk] + kRescale;
+                }
+                if (__builtin_amdgcn_ballot_w64(over) != 0) {
+                    // new maxima: the tile's maximum per head, then rescale what
+                    // has been accumulated with the old ones
+#pragma unroll
+                    for (int j = 0; j < GT; ++j) {
+                        float v = -INFINITY;
+#pragma unroll
+                        for (int kk = 0; kk < NT; ++kk)
+                            if ((base + kk) % GT == j) v = fmaxf(v, x[kk]);
+                        const float m_new = fmaxf(m_run[j], group_max<kWave>(v));
+                        const float alpha = (m_run[j] == -INFINITY) ? 0.0f : fast_exp2(m_run[j] - m_new);
+                        m_run[j] = m_new;
+                        psum[j] *= alpha;
+#pragma unroll
+                        for (int e = 0; e < C::EPL; ++e) acc[j][e] *= alpha;
+#pragma unroll
+                        for (int kk = 0; kk < NT; ++kk)
+                            if ((base + kk) % GT == j) {
+                                l_lane[kk] *= alpha;
+                                m_lane[kk] = m_new;
+                            }
+                    }
+                }
+#pragma unroll
+                for (int kk = 0; kk < NT; ++kk) {
                     if (kk < valid) {
-                        const int i = idx / GT, j = idx - (idx / GT) * GT;
-                        const int r = i * C::RPL + row_lane;
-                        const int tok = tbase + b * kBlk + r;
-                        const bool ok = blk_ok && tok >= c0 && tok < c1;
-                        lg[(it * kBlk + r) * C::GTP + j] = ok ? part[kk] * a.scale_log2 : -INFINITY;
+                        const int idx = base + kk;
+                        const int j = idx % GT;
+                        const int r = (idx / GT) * C::RPL + row_lane;
+                        const float p = (x[kk] == -INFINITY) ? 0.0f : fast_exp2(x[kk] - m_lane[kk]);
+                        if (owner) l_lane[kk] += p;
+                        lp[r * C::GTP + j] = p;
                     }
                 }
             };
-            {
-                int it = 0;
-                for (; it + 1 < nbw; ++it) {
-                    load_tile<KV, D, GT>(nxt, a.k_pool, a.k_scale, tile_of(it + 1, g), lane);
-                    k_step(cur, it);
-                    cur = nxt;
-                }
-                if (it < nbw) {
-                    // the first V tile streams in during the last K step and the softmax
-                    load_tile<KV, D, GT>(nxt, a.v_pool, a.v_scale, tile_of(0, g), lane);
-                    k_step(cur, it);
-                    cur = nxt;
-                }
-            }
-            // LDS operations of one wave take effect in program order; this keeps
-            // the compiler from moving the reads below above the writes above.
-            asm volatile("" ::: "memory");
 
-            // ---- softmax statistics of this wave's keys of the chunk (no other wave involved)
-            const int T = nbw * kBlk;
-            float mloc[GT];
-#pragma unroll
-            for (int j = 0; j < GT; ++j) mloc[j] = -INFINITY;
-            for (int t = lane; t < T; t += kWave)
-#pragma unroll
-                for (int j = 0; j < GT; ++j) mloc[j] = fmaxf(mloc[j], lg[t * C::GTP + j]);
-            float m_new[GT], lloc[GT];
-#pragma unroll
-            for (int j = 0; j < GT; ++j) {
-                m_new[j] = fmaxf(m_run[j], group_max<kWave>(mloc[j]));
-                lloc[j] = 0.0f;
-            }
-            for (int t = lane; t < T; t += kWave)
-#pragma unroll
-                for (int j = 0; j < GT; ++j) {
-                    const float x = lg[t * C::GTP + j];
-                    const float p = (x == -INFINITY) ? 0.0f : fast_exp2(x - m_new[j]);
-                    lg[t * C::GTP + j] = p;
-                    lloc[j] += p;
-                }
-            asm volatile("" ::: "memory");
-#pragma unroll
-            for (int j = 0; j < GT; ++j) {
-                const float alpha = (m_run[j] == -INFINITY) ? 0.0f : fast_exp2(m_run[j] - m_new[j]);
-                l_run[j] = l_run[j] * alpha + group_sum<kWave>(lloc[j]);
-                m_run[j] = m_new[j];
-                psum[j] *= alpha;
-#pragma unroll
-                for (int e = 0; e < C::EPL; ++e) acc[j][e] *= alpha;
-            }
-
-            // ---- phase 2: V tiles, p * v, one tile of lookahead (last iteration peeled)
+            // ---- V tile: acc += p * v over its 16 keys
             auto v_step = [&](const Tile<KV, D, GT>& t, int it) {
                 const int b = wave + kWaves * it;
                 const bool blk_ok = (okmask >> it) & 1;
@@ -438,7 +494,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
 #pragma unroll
                         for (int w = 0; w < C::WORDS; ++w) wv.w[w] = row_ok ? wv.w[w] : 0u;
                     }
-                    const float* pp = &lg[(it * kBlk + r) * C::GTP];
+                    const float* pp = &lp[r * C::GTP];
                     float p[C::GTP];
                     const f32x4_t p0 = *reinterpret_cast<const f32x4_t*>(pp);
                     p[0] = p0[0]; p[1] = p0[1]; p[2] = p0[2]; p[3] = p0[3];
@@ -461,36 +517,45 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
                         for (int e = 0; e < C::EPL; ++e) acc[j][e] = fmaf(p[j], x[e], acc[j][e]);
                 }
             };
-            {
-                int it = 0;
-                for (; it + 1 < nbw; ++it) {
-                    load_tile<KV, D, GT>(nxt, a.v_pool, a.v_scale, tile_of(it + 1, g), lane);
-                    v_step(cur, it);
-                    cur = nxt;
-                }
-                if (it < nbw) v_step(cur, it);
+
+            int it = 0;
+            for (; it + 1 < nbw; ++it) {
+                k_step(tk, it);
+                load_tile<KV, D, GT>(tk, a.k_pool, a.k_scale, tile_of(it + 1, g), lane);
+                __builtin_amdgcn_sched_barrier(0);
+                v_step(tv, it);
+                load_tile<KV, D, GT>(tv, a.v_pool, a.v_scale, tile_of(it + 1, g), lane);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            // the next chunk's logits overwrite this chunk's probabilities
-            asm volatile("" ::: "memory");
-            if (c1 >= I.t1 && item + (int)gridDim.x < total) {
-                // last chunk: start the next item's loads now (Q, block ids, first K tile);
-                // they complete while this item is combined and written
-                nextI = item_info(item + gridDim.x);
-                load_q(nextI);
-                if (nextI.t0 < nextI.t1) {
-                    const int n0 = nextI.t0, n1 = chunk_end(n0, nextI.t1);
-                    const int nbw_n = blocks_of_wave(n0, n1);
-                    chunk_ids(nextI, n0 / kBlk, nbw_n);
-                    if (nbw_n > 0) load_tile<KV, D, GT>(cur, a.k_pool, a.k_scale, tile_of(0, nextI.g), lane);
-                }
-                pre = true;
-            }
+            // the last block of the batch: the stream continues with the first
+            // block of the next batch or item (and that item's Q, which this
+            // item no longer needs once its last K step is done).  Both loads
+            // are unconditional (block 0 when there is no next block): with a
+            // condition on each, the compiler would allow for a K load not
+            // followed by a V load and wait for every load at the next K step.
+            if (nbw > 0) k_step(tk, it);
+            if (!more && have_next) load_q(NI);
+            const int64_t t_n = (int64_t)__builtin_amdgcn_readlane(valid_id(id_n) ? id_n : 0, 0) * a.num_kv_heads + g_n;
+            load_tile<KV, D, GT>(tk, a.k_pool, a.k_scale, t_n, lane);
+            __builtin_amdgcn_sched_barrier(0);
+            if (nbw > 0) v_step(tv, it);
+            load_tile<KV, D, GT>(tv, a.v_pool, a.v_scale, t_n, lane);
+            __builtin_amdgcn_sched_barrier(0);
+            if (any_next) install(id_n);
             c0 = c1;
-        }
-        if (!pre && item + (int)gridDim.x < total) nextI = item_info(item + gridDim.x);
+        } while (c0 < I.t1);
 
         // ---- combine: the lanes of each column, then the waves, each wave's
         // state rescaled to the common maximum
+        float l_run[GT];
+#pragma unroll
+        for (int j = 0; j < GT; ++j) {
+            float v = 0.0f;
+#pragma unroll
+            for (int kk = 0; kk < NT; ++kk)
+                if (kk < tb_valid && (tb_base + kk) % GT == j) v += l_lane[kk];
+            l_run[j] = group_sum<kWave>(v);
+        }
         if constexpr (KV == KV_I8) {
 #pragma unroll
             for (int j = 0; j < GT; ++j)
@@ -519,6 +584,9 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
                 s_ml[parity][wave][0][j] = m_run[j];
                 s_ml[parity][wave][1][j] = l_run[j];
             }
+            // the item after the following one; every wave read this slot
+            // before the previous item's barrier
+            if (dyn && wave == 0) s_next[parity] = following < total ? (int)gridDim.x + claimed : total;
         }
         // One barrier per item: the buffers alternate, so a wave that runs ahead
         // writes the other buffer, and it can only come back to this one after
@@ -555,6 +623,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
             }
         }
         parity ^= 1;
+        I = NI;
     }
 }
 
@@ -623,6 +692,12 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecodeArgs a) {
     }
 }
 
+// Zero the item counter of the next partition launch (a kernel rather than a
+// memset, so the call can be captured in a graph).
+__global__ void decode_reset_kernel(unsigned* ticket) {
+    if (threadIdx.x == 0) *ticket = 0u;
+}
+
 // ---------------------------------------------------------------- host side
 using PartKernel = void (*)(DecodeArgs);
 
@@ -658,7 +733,7 @@ size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t hea
     if (max_partitions <= 0) return 0;
     const size_t slots = (size_t)num_seqs * num_q_heads * max_partitions;
     const size_t ml = (slots * 2 * sizeof(float) + 255) & ~(size_t)255;
-    return ml + slots * head_dim * sizeof(float);
+    return kTicketBytes + ml + slots * head_dim * sizeof(float);
 }
 
 hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
@@ -701,9 +776,10 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
     const int64_t per_seq_items = (int64_t)(merge ? max_parts : 1) * L.num_kv_heads * chunks;
 
     const size_t slots_total = (size_t)L.num_seqs * L.num_q_heads * (merge ? max_parts : 0);
-    float* ml_base = static_cast<float*>(L.workspace);
-    float* o_base = merge ? reinterpret_cast<float*>(static_cast<char*>(L.workspace) +
-                                                     ((slots_total * 2 * sizeof(float) + 255) & ~(size_t)255))
+    unsigned* ticket = merge ? static_cast<unsigned*>(L.workspace) : nullptr;
+    char* ws = merge ? static_cast<char*>(L.workspace) + kTicketBytes : nullptr;
+    float* ml_base = reinterpret_cast<float*>(ws);
+    float* o_base = merge ? reinterpret_cast<float*>(ws + ((slots_total * 2 * sizeof(float) + 255) & ~(size_t)255))
                           : nullptr;
 
     for (int32_t s0 = 0; s0 < L.num_seqs; s0 += kMaxSeqs) {
@@ -717,8 +793,14 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
         b.context_lens = L.context_lens + s0;
         b.part_ml = merge ? ml_base + (int64_t)s0 * L.num_q_heads * max_parts * 2 : nullptr;
         b.part_o = merge ? o_base + (int64_t)s0 * L.num_q_heads * max_parts * L.head_dim : nullptr;
+        b.ticket = ticket;
         const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(resident, (int64_t)n * per_seq_items));
-        hipError_t e = launch(kern, dim3((unsigned)grid), dim3(kThreads), 0, stream, b);
+        hipError_t e = hipSuccess;
+        if (ticket) {
+            e = launch(decode_reset_kernel, dim3(1), dim3(kWave), 0, stream, ticket);
+            if (e != hipSuccess) return e;
+        }
+        e = launch(kern, dim3((unsigned)grid), dim3(kThreads), 0, stream, b);
         if (e != hipSuccess) return e;
         if (merge) {
             if (L.split_event) {
