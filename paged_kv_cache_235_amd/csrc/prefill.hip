@@ -147,37 +147,49 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_chunk_kernel(PrefillArgs 
     const int v_kg = tid / (D / 4);
     u32x4_t kreg[KCH];
     u32x2_t vreg[8];
-    int ids[4];                                 // physical blocks of the tile (0 when invalid)
+    int id0 = 0, id1 = 0, id2 = 0, id3 = 0;     // physical blocks of the tile (0 when invalid)
     int vmask = 0;                              // bit b: block b of the tile holds keys
 
     // The tile's block ids are wave-uniform: read once, before any K/V load,
     // so the 12 loads of a tile issue back to back.
     auto tile_ids = [&](int kt) {
         int m = 0;
+        int got[4];
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const int lb = kt / kBlk + b;
             const int id = lb <= last_blk ? table[lb] : -1;
             const bool ok = id >= 0 && id < a.num_blocks;
-            ids[b] = ok ? id : 0;               // an invalid block reads block 0 and is masked
+            got[b] = ok ? id : 0;               // an invalid block reads block 0 and is masked
             m |= (ok ? 1 : 0) << b;
         }
+        id0 = got[0]; id1 = got[1]; id2 = got[2]; id3 = got[3];
         return m;
     };
-    auto pick = [&](int b) {                    // ids[b] without dynamic register indexing
-        return b == 0 ? ids[0] : b == 1 ? ids[1] : b == 2 ? ids[2] : ids[3];
-    };
+    auto sel = [&](int b) { return b == 0 ? id0 : (b == 1 ? id1 : (b == 2 ? id2 : id3)); };
+    // Each thread's pieces of a tile lie in fixed blocks of the tile: K chunk i
+    // in block (KCH_BLK i + lane-dependent part), the V piece in block
+    // (8 v_kg) / 16.  The block ids are wave-uniform (scalar registers), so
+    // an address is a scalar base plus a 32-bit per-thread offset.
+    const int k_off = ((tid / (D / 8)) % kBlk) * D + (tid % (D / 8)) * 8;     // within the block's head tile
+    const int v_off = ((8 * v_kg) % kBlk) * D + 4 * v_dq;
+    auto blk_base = [&](const uint16_t* pool, int id) { return pool + (int64_t)id * blk_stride + g * head_stride; };
     auto load_tile = [&]() {
 #pragma unroll
         for (int i = 0; i < KCH; ++i) {
-            const int c = tid + kThreads * i;
-            const int key = c / (D / 8), dc = c % (D / 8);
-            kreg[i] = *reinterpret_cast<const u32x4_t*>(
-                a.k_pool + pick(key / kBlk) * blk_stride + g * head_stride + (key % kBlk) * D + dc * 8);
+            // chunk i of this thread is key (tid + 256 i) / (D / 8), in block
+            // (256 i + tid) / KPB = b_lo + tid / KPB
+            constexpr int KPB = kBlk * (D / 8);                 // chunks per block
+            static_assert(kThreads % KPB == 0, "K chunks of a thread stay block-aligned");
+            const int b_lo = (kThreads * i) / KPB;
+            const int id = kThreads == KPB ? sel(b_lo) : sel(b_lo + tid / KPB);
+            kreg[i] = *reinterpret_cast<const u32x4_t*>(blk_base(a.k_pool, id) + k_off);
         }
         if (v_task) {
-            const uint16_t* vp = a.v_pool + pick((8 * v_kg) / kBlk) * blk_stride + g * head_stride +
-                                 ((8 * v_kg) % kBlk) * D + 4 * v_dq;
+            // block of the V piece: (8 v_kg) / 16 = tid / (2 (D / 4))
+            constexpr int TPB = 2 * (D / 4);                    // V threads per block
+            const int id = sel(tid / TPB);
+            const uint16_t* vp = blk_base(a.v_pool, id) + v_off;
 #pragma unroll
             for (int i = 0; i < 8; ++i) vreg[i] = *reinterpret_cast<const u32x2_t*>(vp + i * D);
         }
@@ -191,13 +203,20 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_chunk_kernel(PrefillArgs 
         }
         if (v_task) {
             // zero keys of invalid blocks and unwritten tail slots (>= L): they may hold NaN
-            const bool blk_live = (m >> ((8 * v_kg) / kBlk)) & 1;
             uint32_t w[8][2];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const bool live = blk_live && kt + 8 * v_kg + i < L;
-                w[i][0] = live ? vreg[i][0] : 0u;
-                w[i][1] = live ? vreg[i][1] : 0u;
+                w[i][0] = vreg[i][0];
+                w[i][1] = vreg[i][1];
+            }
+            if (m != 15 || kt + kKeys > L) {    // edge tile (uniform branch)
+                const bool blk_live = (m >> ((8 * v_kg) / kBlk)) & 1;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const bool live = blk_live && kt + 8 * v_kg + i < L;
+                    w[i][0] = live ? w[i][0] : 0u;
+                    w[i][1] = live ? w[i][1] : 0u;
+                }
             }
             // 8 keys x 4 dims -> 4 rows of 8 keys, bf16 -> fp16
 #pragma unroll
@@ -278,18 +297,37 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_chunk_kernel(PrefillArgs 
         }
         const float msub = (m_used == -INFINITY) ? 0.0f : m_used;
         uint32_t pw[2][8];                       // P^T as fp16 pairs: [T][4u + word]
-        float lsum = 0.0f;
+        if (a.scale_log2 > 0.0f) {
+            // a masked score (-inf) scales to -inf and exp2 gives 0 by itself
 #pragma unroll
-        for (int T = 0; T < 2; ++T)
+            for (int T = 0; T < 2; ++T)
 #pragma unroll
-            for (int v = 0; v < 16; v += 2) {
-                const float x0 = sacc[T][v], x1 = sacc[T][v + 1];
-                const float p0 = (x0 == -INFINITY) ? 0.0f : fast_exp2(fmaf(x0, a.scale_log2, -msub));
-                const float p1 = (x1 == -INFINITY) ? 0.0f : fast_exp2(fmaf(x1, a.scale_log2, -msub));
-                lsum += p0 + p1;
-                pw[T][v / 2] = pack_f16x2(p0, p1);
+                for (int v = 0; v < 16; v += 2)
+                    pw[T][v / 2] = pack_f16x2(fast_exp2(fmaf(sacc[T][v], a.scale_log2, -msub)),
+                                              fast_exp2(fmaf(sacc[T][v + 1], a.scale_log2, -msub)));
+        } else {
+            // scale 0: -inf * 0 would be NaN, so masked scores are selected away
+#pragma unroll
+            for (int T = 0; T < 2; ++T)
+#pragma unroll
+                for (int v = 0; v < 16; v += 2) {
+                    const float x0 = sacc[T][v], x1 = sacc[T][v + 1];
+                    const float p0 = (x0 == -INFINITY) ? 0.0f : fast_exp2(fmaf(x0, a.scale_log2, -msub));
+                    const float p1 = (x1 == -INFINITY) ? 0.0f : fast_exp2(fmaf(x1, a.scale_log2, -msub));
+                    pw[T][v / 2] = pack_f16x2(p0, p1);
+                }
+        }
+        // row sum of the fp16 weights -- the values P.V multiplies -- two per dot2
+        {
+            const f16x2_t one = {(_Float16)1.0f, (_Float16)1.0f};
+            float ls0 = 0.0f, ls1 = 0.0f;
+#pragma unroll
+            for (int w = 0; w < 8; ++w) {
+                ls0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pw[0][w]), one, ls0, false);
+                ls1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pw[1][w]), one, ls1, false);
             }
-        l_run += lsum;
+            l_run += ls0 + ls1;
+        }
 
         // ---- O^T += V^T P^T: k-step ks covers keys 16ks..16ks+15 (tile T = ks/2, u = ks%2)
 #pragma unroll
