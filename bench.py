@@ -126,22 +126,25 @@ def bench_decode(args, torch, pkv, workloads, tl):
     print(f"[bench] decode setup done; workspace {ws_bytes / 2**20:.1f} MiB", flush=True)
 
     def step(ev=None):
+        # ev: after-start, after-write, before-partition (library), after-partition (library), end
         if ev:
             ev[0].record()
         pkv.kv_cache_write(new_k, new_v, new_slots, pools["k"], pools["v"])
         if ev:
             ev[1].record()
-            pkv.set_decode_split_event(ev[2])
+            pkv.set_decode_start_event(ev[2])
+            pkv.set_decode_split_event(ev[3])
         pkv.paged_attention_decode(q, pools["k"], pools["v"], bt, lens, case.softmax_scale,
                                    partition_size=case.partition_size, out=out, workspace=workspace)
         if ev:
+            pkv.set_decode_start_event(None)
             pkv.set_decode_split_event(None)
-            ev[3].record()
+            ev[4].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -155,9 +158,10 @@ def bench_decode(args, torch, pkv, workloads, tl):
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(end)
     t_write = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    t_part = np.array([e[1].elapsed_time(e[2]) for e in evs])
-    t_merge = np.array([e[2].elapsed_time(e[3]) for e in evs])
-    t_step = np.array([e[0].elapsed_time(e[3]) for e in evs])
+    t_reset = np.array([e[1].elapsed_time(e[2]) for e in evs])     # work-counter clear + launch gap
+    t_part = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    t_merge = np.array([e[3].elapsed_time(e[4]) for e in evs])
+    t_step = np.array([e[0].elapsed_time(e[4]) for e in evs])
 
     # correctness of the timed configuration, on a sample of sequences
     check = sorted({int(np.argmax(case.seq_lens)), int(np.argmin(case.seq_lens)), 7, 100, 200})
@@ -179,6 +183,7 @@ def bench_decode(args, torch, pkv, workloads, tl):
         "wall_ms_per_step": wall * 1e3 / args.steps,
         "step_bytes": step_bytes,
         "breakdown_us": {"kv_cache_write": float(np.mean(t_write)) * 1e3,
+                         "decode_counter_clear": float(np.mean(t_reset)) * 1e3,
                          "decode_partition": float(np.mean(t_part)) * 1e3,
                          "decode_merge": float(np.mean(t_merge)) * 1e3,
                          "step_median": float(np.median(t_step)) * 1e3,

@@ -201,6 +201,15 @@ const char* pkv_version(void);
  */
 int pkv_profile_set_decode_split_event(void* hip_event);
 
+/*
+ * Profiling aid: while `hip_event` is non-NULL, every decode call on this
+ * thread records the event on its stream immediately before the partition
+ * kernel (after the kernel that clears the work counter), so that with the
+ * split event the partition kernel is timed alone.  Pass NULL to stop.
+ * Always returns PKV_OK.
+ */
+int pkv_profile_set_decode_start_event(void* hip_event);
+
 #ifdef __cplusplus
 }
 #endif

@@ -13,8 +13,9 @@ The library is loaded on first use; there is no CPU fallback.
 """
 from ._binding import (EXPORTS, LIB_PATH, CacheDesc, PagedKVError, cache_desc, decode_workspace_size,
                        kv_cache_write, last_error, load_library, paged_attention_decode,
-                       paged_attention_prefill_chunk, set_decode_split_event, version)
+                       paged_attention_prefill_chunk, set_decode_split_event, set_decode_start_event,
+                       version)
 
 __all__ = ["EXPORTS", "LIB_PATH", "CacheDesc", "PagedKVError", "cache_desc", "decode_workspace_size",
            "kv_cache_write", "last_error", "load_library", "paged_attention_decode",
-           "paged_attention_prefill_chunk", "set_decode_split_event", "version"]
+           "paged_attention_prefill_chunk", "set_decode_split_event", "set_decode_start_event", "version"]

@@ -23,7 +23,7 @@ STATUS = {0: "PKV_OK", 1: "PKV_EINVAL", 2: "PKV_EUNSUPPORTED", 3: "PKV_EWORKSPAC
 # every symbol include/pagedkv.h declares
 EXPORTS = ("kv_cache_write", "paged_attention_decode_workspace_size", "paged_attention_decode",
            "paged_attention_prefill_chunk", "pkv_last_error", "pkv_version",
-           "pkv_profile_set_decode_split_event")
+           "pkv_profile_set_decode_split_event", "pkv_profile_set_decode_start_event")
 
 
 class PagedKVError(RuntimeError):
@@ -69,6 +69,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.pkv_version.argtypes = []
             lib.pkv_profile_set_decode_split_event.restype = ctypes.c_int
             lib.pkv_profile_set_decode_split_event.argtypes = [P]
+            lib.pkv_profile_set_decode_start_event.restype = ctypes.c_int
+            lib.pkv_profile_set_decode_start_event.argtypes = [P]
             _lib = lib
     return _lib
 
@@ -240,6 +242,15 @@ def set_decode_split_event(event) -> None:
         event.record()          # torch creates the HIP event on first record
     ptr = None if event is None else ctypes.c_void_p(event.cuda_event)
     load_library().pkv_profile_set_decode_split_event(ptr)
+
+
+def set_decode_start_event(event) -> None:
+    """Profiling aid: record ``event`` (torch.cuda.Event or None) right before
+    the decode partition kernel of later decode calls on this thread."""
+    if event is not None and not event.cuda_event:
+        event.record()
+    ptr = None if event is None else ctypes.c_void_p(event.cuda_event)
+    load_library().pkv_profile_set_decode_start_event(ptr)
 
 
 def last_error() -> str:

@@ -800,6 +800,10 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
             e = launch(decode_reset_kernel, dim3(1), dim3(kWave), 0, stream, ticket);
             if (e != hipSuccess) return e;
         }
+        if (L.start_event) {
+            e = hipEventRecord(L.start_event, stream);
+            if (e != hipSuccess) return e;
+        }
         e = launch(kern, dim3((unsigned)grid), dim3(kThreads), 0, stream, b);
         if (e != hipSuccess) return e;
         if (merge) {

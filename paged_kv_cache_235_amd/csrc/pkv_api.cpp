@@ -18,6 +18,7 @@ namespace {
 
 thread_local std::string g_error;
 thread_local hipEvent_t g_split_event = nullptr;
+thread_local hipEvent_t g_start_event = nullptr;
 
 int fail(int status, const char* fmt, ...) {
     char buf[512];
@@ -131,6 +132,11 @@ const char* pkv_version(void) { return "libpagedkv 0.1 (gfx950)"; }
 
 int pkv_profile_set_decode_split_event(void* hip_event) {
     g_split_event = static_cast<hipEvent_t>(hip_event);
+    return PKV_OK;
+}
+
+int pkv_profile_set_decode_start_event(void* hip_event) {
+    g_start_event = static_cast<hipEvent_t>(hip_event);
     return PKV_OK;
 }
 
@@ -271,6 +277,7 @@ int paged_attention_decode(const pkv_cache_desc* cache, const void* q, int32_t q
     L.partition_size = partition_size;
     L.workspace = workspace;
     L.split_event = g_split_event;
+    L.start_event = g_start_event;
     const hipError_t e = pkv::launch_decode(L, st);
     return e == hipSuccess ? PKV_OK : hip_fail(e, "paged_attention_decode launch");
 }

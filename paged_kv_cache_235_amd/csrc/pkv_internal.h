@@ -58,6 +58,7 @@ struct DecodeLaunch {
     int32_t partition_size;    // 0: single pass
     void* workspace;
     hipEvent_t split_event;    // recorded between the two kernels when non-null
+    hipEvent_t start_event;    // recorded right before the partition kernel when non-null
 };
 // Number of partition slots per (sequence, head) in the workspace (0 if no merge).
 int32_t decode_max_partitions(int32_t max_blocks_per_seq, int32_t block_size, int32_t partition_size);
