@@ -248,16 +248,30 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_chunk_kernel(PrefillArgs 
             load_tile();
         }
 
-        // ---- S^T = K Q^T for the wave's 32 rows: two 32-key halves
+        // ---- S^T = K Q^T for the wave's 32 rows: two 32-key halves, their MFMA
+        // chains interleaved (independent accumulators) and the next k-step's
+        // K operands read from LDS before the current k-step's MFMAs issue
         f32x16_t sacc[2];
 #pragma unroll
-        for (int T = 0; T < 2; ++T) {
+        for (int T = 0; T < 2; ++T)
 #pragma unroll
             for (int v = 0; v < 16; ++v) sacc[T][v] = 0.0f;
+        {
+            const uint16_t* kr0 = &s_k[(lane & 31) * KS + 8 * h];
+            const uint16_t* kr1 = kr0 + 32 * KS;
+            u32x4_t k0 = *reinterpret_cast<const u32x4_t*>(kr0);
+            u32x4_t k1 = *reinterpret_cast<const u32x4_t*>(kr1);
 #pragma unroll
             for (int ks = 0; ks < DK; ++ks) {
-                const u32x4_t kv = *reinterpret_cast<const u32x4_t*>(&s_k[(32 * T + (lane & 31)) * KS + 16 * ks + 8 * h]);
-                sacc[T] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), qf[ks], sacc[T], 0, 0, 0);
+                u32x4_t n0 = k0, n1 = k1;
+                if (ks + 1 < DK) {
+                    n0 = *reinterpret_cast<const u32x4_t*>(kr0 + 16 * (ks + 1));
+                    n1 = *reinterpret_cast<const u32x4_t*>(kr1 + 16 * (ks + 1));
+                }
+                sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k0), qf[ks], sacc[0], 0, 0, 0);
+                sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k1), qf[ks], sacc[1], 0, 0, 0);
+                k0 = n0;
+                k1 = n1;
             }
         }
 
@@ -329,7 +343,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_chunk_kernel(PrefillArgs 
             l_run += ls0 + ls1;
         }
 
-        // ---- O^T += V^T P^T: k-step ks covers keys 16ks..16ks+15 (tile T = ks/2, u = ks%2)
+        // ---- O^T += V^T P^T: k-step ks covers keys 16ks..16ks+15 (tile T = ks/2, u = ks%2).
+        // Lane reads V^T row d = 32 nt + (lane & 31), key group g = 2 ks + h, at
+        // vt_col(d, g) = 8 * (g ^ ((d >> 4) & 7)) = 16 (ks ^ nt) + 8 (h ^ bit 4 of lane):
+        // one per-lane base plus a compile-time offset per (nt, ks).
+        const uint16_t* vt_base = &s_vt[(lane & 31) * kVtStride + 8 * (h ^ ((lane >> 4) & 1))];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const int T = ks >> 1, u = ks & 1;
@@ -338,8 +356,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_chunk_kernel(PrefillArgs 
             pb[2] = pw[T][4 * u + 2]; pb[3] = pw[T][4 * u + 3];
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
-                const int d = 32 * nt + (lane & 31);
-                const u32x4_t vv = *reinterpret_cast<const u32x4_t*>(&s_vt[d * kVtStride + vt_col(d, 2 * ks + h)]);
+                const u32x4_t vv = *reinterpret_cast<const u32x4_t*>(
+                    vt_base + 32 * nt * kVtStride + 16 * ((ks ^ nt) & 7));
                 o[nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(vv), as_f16x8(pb), o[nt], 0, 0, 0);
             }
         }
