@@ -387,6 +387,333 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_chunk_kernel(PrefillArgs 
         }
 }
 
+// ---------------------------------------------------------------------------
+// Pipelined variant: W waves (32 query rows each) share double-buffered K/V
+// tiles, and each wave issues the next tile's S^T = K Q^T MFMAs before this
+// tile's softmax, so the matrix cores work while the VALU computes exp2.
+template <int D, int W, bool ZS>
+__global__ __launch_bounds__(64 * W) void prefill_pipe_kernel(PrefillArgs a) {
+    constexpr int NTH = 64 * W;                 // threads
+    constexpr int ROWS = 32 * W;                // query rows per workgroup
+    constexpr int KS = D + 8;                   // halfwords per K row in LDS
+    constexpr int DK = D / 16;                  // k-steps of Q.K^T
+    constexpr int NT = D / 32;                  // 32-wide d tiles of the output
+    constexpr int KCH = kKeys * (D / 8) / NTH;  // 16-byte K chunks staged per thread
+    constexpr int KPB = kBlk * (D / 8);         // K chunks per block
+    constexpr int VPIECES = 8 * (D / 2);        // (8-key group, 2 dims) pieces of V per tile
+    constexpr float kRescale = 8.0f;            // rescale O only when a row max grows by > 2^8
+    static_assert(KCH >= 1 && NTH % KPB == 0 && VPIECES <= NTH, "staging shape");
+    __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kKeys * KS];
+    __shared__ __attribute__((aligned(16))) uint16_t s_vt[2][D * kVtStride];   // V^T as fp16
+
+    // ---- work item: XCD-major so that one (sequence, head) stays on one XCD
+    const int per_xcd = (a.total + kXcds - 1) / kXcds;
+    const int w_idx = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+    if (w_idx >= a.total) return;
+    const int mt = w_idx % a.m_tiles;
+    const int g = (w_idx / a.m_tiles) % a.num_kv_heads;
+    const int s = w_idx / (a.m_tiles * a.num_kv_heads);
+    const int G = a.group;
+    const int q0 = a.cu_q_lens[s];
+    const int C = a.cu_q_lens[s + 1] - q0;
+    const int L = min(a.seq_lens[s], a.max_blocks * kBlk);
+    const int nrows = C * G;
+    const int r0 = mt * ROWS;
+    if (r0 >= nrows || C <= 0 || C > L) return;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int h = lane >> 5;                    // lane half
+    const int base_pos = L - C;                 // position of chunk token 0
+    const int p_min = base_pos + r0 / G;
+    const int p_max = base_pos + (min(nrows, r0 + ROWS) - 1) / G;
+
+    // ---- this lane's query row and its Q fragment (B operand of S^T = K Q^T)
+    const int row = r0 + wave * 32 + (lane & 31);
+    const bool row_ok = row < nrows;
+    const int tok = row_ok ? row / G : 0;
+    const int jh = row_ok ? row - tok * G : 0;
+    const int p_row = row_ok ? base_pos + tok : p_max;
+    bf16x8_t qf[DK];
+    {
+        const uint16_t* qp = a.q + ((int64_t)(q0 + tok) * a.num_q_heads + g * G + jh) * D + 8 * h;
+#pragma unroll
+        for (int ks = 0; ks < DK; ++ks) {
+            u32x4_t v = {0u, 0u, 0u, 0u};
+            if (row_ok) v = *reinterpret_cast<const u32x4_t*>(qp + 16 * ks);
+            qf[ks] = as_bf16x8(v);
+        }
+    }
+
+    f32x16_t o[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[nt][v] = 0.0f;
+    float m_used = -INFINITY;    // max the weights are taken against (log2 units)
+    float l_run = 0.0f;          // this lane's share of the row sum
+
+    const int k_lo = (a.window > 0) ? max(0, p_min - a.window + 1) : 0;
+    const int kt_first = (k_lo / kKeys) * kKeys;
+    const int n_tiles = kt_first <= p_max ? (p_max - kt_first) / kKeys + 1 : 0;
+    const int last_blk = (L - 1) / kBlk;        // last logical block with keys
+    const int32_t* table = a.block_tables + (int64_t)s * a.max_blocks;
+    const int64_t head_stride = (int64_t)kBlk * D;          // elements per (block, head) tile
+    const int64_t blk_stride = (int64_t)a.num_kv_heads * head_stride;
+
+    // ---- staging roles: KCH 16-byte K chunks and (if any) one V piece per thread
+    //  K chunk c = tid + NTH i: key c / (D/8), dims (c % (D/8)) * 8 .. +8
+    //  V piece t = tid: dims 2 (t % (D/2)), +1 of keys 8 (t / (D/2)) .. +8
+    const bool v_task = tid < VPIECES;
+    const int v_dp = tid % (D / 2);
+    const int v_kg = (tid / (D / 2)) & 7;
+    const int k_off = ((tid / (D / 8)) % kBlk) * D + (tid % (D / 8)) * 8;
+    const int v_off = ((8 * v_kg) % kBlk) * D + 2 * v_dp;
+    u32x4_t kreg[KCH];
+    uint32_t vreg[8];
+    int id0 = 0, id1 = 0, id2 = 0, id3 = 0;     // physical blocks of the staged tile (0 when invalid)
+
+    auto kt_of = [&](int t) { return kt_first + kKeys * t; };
+    auto tile_ids = [&](int kt) {               // block ids of a tile (wave-uniform): bit b = block b valid
+        int m = 0;
+        int got[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int lb = kt / kBlk + b;
+            const int id = lb <= last_blk ? table[lb] : -1;
+            const bool ok = id >= 0 && id < a.num_blocks;
+            got[b] = ok ? id : 0;               // an invalid block reads block 0 and is masked
+            m |= (ok ? 1 : 0) << b;
+        }
+        id0 = got[0]; id1 = got[1]; id2 = got[2]; id3 = got[3];
+        return m;
+    };
+    auto sel = [&](int b) { return b == 0 ? id0 : (b == 1 ? id1 : (b == 2 ? id2 : id3)); };
+    auto blk_base = [&](const uint16_t* pool, int id) { return pool + (int64_t)id * blk_stride + g * head_stride; };
+    auto load_tile = [&]() {
+#pragma unroll
+        for (int i = 0; i < KCH; ++i) {
+            const int id = sel((NTH * i) / KPB + tid / KPB);
+            kreg[i] = *reinterpret_cast<const u32x4_t*>(blk_base(a.k_pool, id) + k_off);
+        }
+        if (v_task) {
+            const uint16_t* vp = blk_base(a.v_pool, sel(v_kg / 2)) + v_off;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) vreg[i] = *reinterpret_cast<const uint32_t*>(vp + i * D);
+        }
+    };
+    auto store_tile = [&](int buf, int kt, int m) {
+#pragma unroll
+        for (int i = 0; i < KCH; ++i) {
+            const int c = tid + NTH * i;
+            const int key = c / (D / 8), dc = c % (D / 8);
+            *reinterpret_cast<u32x4_t*>(&s_k[buf][swap23(key) * KS + dc * 8]) = kreg[i];
+        }
+        if (v_task) {
+            uint32_t w[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) w[i] = vreg[i];
+            if (m != 15 || kt + kKeys > L) {    // edge tile (uniform branch): zero dead keys, they may hold NaN
+                const bool blk_live = (m >> (v_kg / 2)) & 1;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) w[i] = (blk_live && kt + 8 * v_kg + i < L) ? w[i] : 0u;
+            }
+            // 8 keys x 2 dims -> 2 rows of 8 keys, bf16 -> fp16
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                u32x4_t r;
+#pragma unroll
+                for (int mm = 0; mm < 4; ++mm)
+                    r[mm] = e ? pack_f16x2(bf16hi(w[2 * mm]), bf16hi(w[2 * mm + 1]))
+                              : pack_f16x2(bf16lo(w[2 * mm]), bf16lo(w[2 * mm + 1]));
+                const int d = 2 * v_dp + e;
+                *reinterpret_cast<u32x4_t*>(&s_vt[buf][d * kVtStride + vt_col(d, v_kg)]) = r;
+            }
+        }
+    };
+
+    // S^T of a staged tile for the wave's 32 rows: two 32-key halves, their MFMA
+    // chains interleaved and the K operands read a k-step ahead
+    auto compute_s = [&](f32x16_t* S, int buf) {
+#pragma unroll
+        for (int T = 0; T < 2; ++T)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) S[T][v] = 0.0f;
+        const uint16_t* kr0 = &s_k[buf][(lane & 31) * KS + 8 * h];
+        const uint16_t* kr1 = kr0 + 32 * KS;
+        u32x4_t k0 = *reinterpret_cast<const u32x4_t*>(kr0);
+        u32x4_t k1 = *reinterpret_cast<const u32x4_t*>(kr1);
+#pragma unroll
+        for (int ks = 0; ks < DK; ++ks) {
+            u32x4_t n0 = k0, n1 = k1;
+            if (ks + 1 < DK) {
+                n0 = *reinterpret_cast<const u32x4_t*>(kr0 + 16 * (ks + 1));
+                n1 = *reinterpret_cast<const u32x4_t*>(kr1 + 16 * (ks + 1));
+            }
+            S[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k0), qf[ks], S[0], 0, 0, 0);
+            S[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k1), qf[ks], S[1], 0, 0, 0);
+            k0 = n0;
+            k1 = n1;
+        }
+    };
+
+    // masks, online softmax and O^T += V^T P^T for tile t (scores in S, V in buf);
+    // the next tile's S^T MFMAs (into S_nxt, from buffer buf ^ 1) are issued in
+    // the same basic block as the exp2 work so the two overlap.  On the last
+    // tile that buffer holds stale data: the MFMAs still read in-bounds LDS and
+    // their result is never used.
+    auto finish_tile = [&](f32x16_t* S, f32x16_t* S_nxt, int buf, int kt, int tmask) {
+        // masks (edge tiles only): key of accumulator v = kt + 32T + 16(v/8) + 8h + v%8
+        const bool full = tmask == 15 && kt + kKeys - 1 <= p_min && (a.window <= 0 || kt >= p_max - a.window + 1);
+        if (!full) {
+#pragma unroll
+            for (int T = 0; T < 2; ++T)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int key = kt + 32 * T + 16 * (v / 8) + 8 * h + (v % 8);
+                    const bool vis = ((tmask >> ((key - kt) / kBlk)) & 1) && key <= p_row &&
+                                     (a.window <= 0 || key > p_row - a.window);
+                    S[T][v] = vis ? S[T][v] : -INFINITY;
+                }
+        }
+        // online softmax for the row (lane-local + lane^32), lazy rescale
+        float mt_ = -INFINITY;
+#pragma unroll
+        for (int T = 0; T < 2; ++T)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) mt_ = fmaxf(mt_, S[T][v]);
+        mt_ = fmaxf(mt_, __shfl_xor(mt_, 32, kWave));
+        const float m_tile = mt_ == -INFINITY ? -INFINITY : mt_ * a.scale_log2;
+        const bool grow = m_tile > m_used + kRescale || (m_used == -INFINITY && m_tile != -INFINITY);
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+            const float m_new = grow ? m_tile : m_used;
+            const float alpha = (m_used == -INFINITY) ? 0.0f : fast_exp2(m_used - m_new);
+            m_used = m_new;
+            const float f = grow ? alpha : 1.0f;
+            l_run *= f;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) o[nt][v] *= f;
+        }
+        const float msub = (m_used == -INFINITY) ? 0.0f : m_used;
+        compute_s(S_nxt, buf ^ 1);
+        uint32_t pw[2][8];                       // P^T as fp16 pairs: [T][4u + word]
+        if constexpr (!ZS) {
+            // a masked score (-inf) scales to -inf and exp2 gives 0 by itself
+#pragma unroll
+            for (int T = 0; T < 2; ++T)
+#pragma unroll
+                for (int v = 0; v < 16; v += 2)
+                    pw[T][v / 2] = pack_f16x2(fast_exp2(fmaf(S[T][v], a.scale_log2, -msub)),
+                                              fast_exp2(fmaf(S[T][v + 1], a.scale_log2, -msub)));
+        } else {
+            // scale 0: -inf * 0 would be NaN, so masked scores are selected away
+#pragma unroll
+            for (int T = 0; T < 2; ++T)
+#pragma unroll
+                for (int v = 0; v < 16; v += 2) {
+                    const float x0 = S[T][v], x1 = S[T][v + 1];
+                    const float p0 = (x0 == -INFINITY) ? 0.0f : fast_exp2(fmaf(x0, a.scale_log2, -msub));
+                    const float p1 = (x1 == -INFINITY) ? 0.0f : fast_exp2(fmaf(x1, a.scale_log2, -msub));
+                    pw[T][v / 2] = pack_f16x2(p0, p1);
+                }
+        }
+        // row sum of the fp16 weights -- the values P.V multiplies -- two per dot2
+        {
+            const f16x2_t one = {(_Float16)1.0f, (_Float16)1.0f};
+            float ls0 = 0.0f, ls1 = 0.0f;
+#pragma unroll
+            for (int w = 0; w < 8; ++w) {
+                ls0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pw[0][w]), one, ls0, false);
+                ls1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pw[1][w]), one, ls1, false);
+            }
+            l_run += ls0 + ls1;
+        }
+        // O^T += V^T P^T: k-step ks covers keys 16ks..16ks+15 (tile T = ks/2, u = ks%2);
+        // V^T row d = 32 nt + (lane & 31), key group 2 ks + h, at one base + constants
+        const uint16_t* vt_base = &s_vt[buf][(lane & 31) * kVtStride + 8 * (h ^ ((lane >> 4) & 1))];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int T = ks >> 1, u = ks & 1;
+            u32x4_t pb;
+            pb[0] = pw[T][4 * u + 0]; pb[1] = pw[T][4 * u + 1];
+            pb[2] = pw[T][4 * u + 2]; pb[3] = pw[T][4 * u + 3];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const u32x4_t vv = *reinterpret_cast<const u32x4_t*>(
+                    vt_base + 32 * nt * kVtStride + 16 * ((ks ^ nt) & 7));
+                o[nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(vv), as_f16x8(pb), o[nt], 0, 0, 0);
+            }
+        }
+    };
+
+    // ---- prologue: tiles 0 and 1 staged (buffers 0 and 1), S of tile 0, tile 2 in registers
+    int mk0 = 0, mk1 = 0, mk2 = 0;              // masks of tiles t, t + 1, t + 2 (t + 2: in registers)
+    f32x16_t sa[2], sb[2];
+    if (n_tiles > 0) {
+        mk0 = tile_ids(kt_of(0));
+        load_tile();
+        store_tile(0, kt_of(0), mk0);
+    }
+    if (n_tiles > 1) {
+        mk1 = tile_ids(kt_of(1));
+        load_tile();
+    }
+    __syncthreads();                            // tile 0 visible
+    if (n_tiles > 0) compute_s(sa, 0);
+    if (n_tiles > 1) store_tile(1, kt_of(1), mk1);
+    if (n_tiles > 2) {
+        mk2 = tile_ids(kt_of(2));
+        load_tile();
+    }
+    __syncthreads();                            // tile 1 visible
+
+    // ---- steady state: tile t in buffer t & 1 with its S in hand; tile t + 1 in
+    // the other buffer; tile t + 2 in registers
+    auto step = [&](f32x16_t* s_cur, f32x16_t* s_nxt, int t) {
+        const int buf = t & 1;
+        finish_tile(s_cur, s_nxt, buf, kt_of(t), mk0);
+        __syncthreads();                        // every wave is done with buffer buf
+        if (t + 2 < n_tiles) store_tile(buf, kt_of(t + 2), mk2);
+        __syncthreads();                        // tile t + 2 visible
+        mk0 = mk1;
+        mk1 = mk2;
+        if (t + 3 < n_tiles) {                  // fetch tile t + 3 while t + 1 is used
+            mk2 = tile_ids(kt_of(t + 3));
+            load_tile();
+        }
+    };
+    for (int t = 0; t < n_tiles; t += 2) {
+        step(sa, sb, t);
+        if (t + 1 < n_tiles) step(sb, sa, t + 1);
+    }
+
+    // ---- normalise and store: lane holds d = 32nt + 8(v/4) + 4h + v%4 of its row
+    const float l_row = l_run + __shfl_xor(l_run, 32, kWave);
+    if (!row_ok) return;
+    const float inv = l_row > 0.0f ? 1.0f / l_row : 0.0f;
+    const int64_t obase = ((int64_t)(q0 + tok) * a.num_q_heads + g * G + jh) * D;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+            const int d = 32 * nt + 8 * v4 + 4 * h;
+            const float r0_ = o[nt][4 * v4 + 0] * inv, r1_ = o[nt][4 * v4 + 1] * inv;
+            const float r2_ = o[nt][4 * v4 + 2] * inv, r3_ = o[nt][4 * v4 + 3] * inv;
+            if (a.out_bf16) {
+                u32x2_t pk;
+                pk[0] = pack_bf16x2(r0_, r1_);
+                pk[1] = pack_bf16x2(r2_, r3_);
+                *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(a.out) + obase + d) = pk;
+            } else {
+                f32x4_t fv = {r0_, r1_, r2_, r3_};
+                *reinterpret_cast<f32x4_t*>(static_cast<float*>(a.out) + obase + d) = fv;
+            }
+        }
+}
+
 }  // namespace
 
 hipError_t launch_prefill(const PrefillLaunch& L, hipStream_t stream) {
@@ -404,8 +731,10 @@ hipError_t launch_prefill(const PrefillLaunch& L, hipStream_t stream) {
     a.group = L.num_q_heads / L.num_kv_heads;
     a.num_blocks = L.num_blocks;
     a.max_blocks = L.max_blocks_per_seq;
+    constexpr int kPipeWaves = 8;
+    constexpr int kPipeRows = 32 * kPipeWaves;
     const int64_t rows = (int64_t)L.max_q_len * a.group;
-    a.m_tiles = (int32_t)((rows + kRows - 1) / kRows);
+    a.m_tiles = (int32_t)((rows + kPipeRows - 1) / kPipeRows);
     const int64_t total = (int64_t)L.num_seqs * L.num_kv_heads * a.m_tiles;
     if (total > INT32_MAX / 2) return hipErrorInvalidValue;
     a.total = (int32_t)total;
@@ -413,9 +742,13 @@ hipError_t launch_prefill(const PrefillLaunch& L, hipStream_t stream) {
     a.scale_log2 = L.softmax_scale * kLog2e;
     a.out_bf16 = L.out_bf16;
     const int64_t grid = ((total + kXcds - 1) / kXcds) * kXcds;
+    const dim3 g3((unsigned)grid), b3(64 * kPipeWaves);
+    const bool zs = !(a.scale_log2 > 0.0f);
     if (L.head_dim == 64)
-        return launch(prefill_chunk_kernel<64>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
-    return launch(prefill_chunk_kernel<128>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+        return zs ? launch(prefill_pipe_kernel<64, kPipeWaves, true>, g3, b3, 0, stream, a)
+                  : launch(prefill_pipe_kernel<64, kPipeWaves, false>, g3, b3, 0, stream, a);
+    return zs ? launch(prefill_pipe_kernel<128, kPipeWaves, true>, g3, b3, 0, stream, a)
+              : launch(prefill_pipe_kernel<128, kPipeWaves, false>, g3, b3, 0, stream, a);
 }
 
 }  // namespace pkv
