@@ -276,7 +276,7 @@ def bench_prefill(args, torch, pkv, workloads, tl):
                         "contexts, 32 q / 8 kv heads, head_dim 128, bf16, causal + window 4096",
             "us_per_call": round(sec * 1e6, 2), "us_p10": round(float(np.percentile(t, 10)) * 1e3, 2),
             "us_p90": round(float(np.percentile(t, 90)) * 1e3, 2),
-            "roofline": {"kernel": "prefill_chunk_kernel<D=128>", "bound": "mfma", "achieved": round(tf, 1),
+            "roofline": {"kernel": "prefill_pipe_kernel<D=128, 8 waves>", "bound": "mfma", "achieved": round(tf, 1),
                          "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
                          "traffic": read_traffic("prefill_window", "prefill.hip"),

@@ -15,20 +15,26 @@
 // converted from bf16 to fp16 as it is staged; that is exact for
 // 2^-14 <= |v| <= 65504 (smaller values keep an absolute error below 2^-25;
 // larger ones are outside what this path supports).
-//  * A workgroup (4 waves) owns 128 rows of one (sequence, KV head): rows are
-//    (chunk token, query head of the group) pairs, so all G heads of a group
-//    share every K/V tile the workgroup stages.  Each wave owns 32 rows.
+//  * A workgroup (8 waves, one per CU) owns 256 rows of one (sequence, KV
+//    head): rows are (chunk token, query head of the group) pairs, so all G
+//    heads of a group share every K/V tile the workgroup stages.  Each wave
+//    owns 32 rows; its Q fragment stays in registers.
 //  * Keys come in tiles of 64 (four 16-token blocks gathered through the
-//    block table) staged in LDS: K row-major, V transposed.  Tiles wholly
-//    outside every row's causal/window range are never visited; masks are
-//    applied only on edge tiles, by selection.
+//    block table), staged through registers into two LDS buffers: K
+//    row-major, V transposed.  Tiles wholly outside every row's
+//    causal/window range are never visited; masks are applied only on edge
+//    tiles, by selection.
 //  * Each wave computes S^T = K Q^T, so one lane's accumulators hold one
 //    query row's scores: the row max/sum are lane-local plus one exchange
 //    with lane^32.  K rows are staged with bits 2 and 3 of the key index
 //    swapped, which makes each lane's 8 consecutive accumulators 8
-//    consecutive keys: converted to bf16 they are directly the B operand of
+//    consecutive keys: converted to fp16 they are directly the B operand of
 //    O^T += V^T P^T, and V^T is read with one 16-byte LDS load per operand.
-//  * Online softmax in fp32 with exp2 (scale * log2 e folded in).
+//  * Software pipeline: while a wave exponentiates tile t, the MFMAs of tile
+//    t + 1's S^T are already issued (same basic block), so the matrix cores
+//    and the VALU work at once; tile t + 2 is in registers on its way to LDS.
+//  * Online softmax in fp32 with exp2 (scale * log2 e folded in) and a lazy
+//    rescale (the output is rescaled only when a row maximum grows by > 2^8).
 //  * Workgroups of one (sequence, KV head) are placed on the same XCD so the
 //    K/V tiles they all read stay in that XCD's L2.
 #include "pkv_internal.h"
@@ -38,8 +44,6 @@ namespace pkv {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kRows = 128;              // query rows per workgroup
 constexpr int kKeys = 64;               // keys per tile
 constexpr int kBlk = 16;
 constexpr int kVtStride = kKeys + 8;    // halfwords per V^T row (16-byte aligned)
@@ -73,324 +77,8 @@ __device__ __forceinline__ f16x8_t as_f16x8(const u32x4_t& v) { return __builtin
 // (rows d..d+15 of one group) at one pass per 16 lanes.
 __device__ __forceinline__ int vt_col(int d, int g) { return ((g ^ ((d >> 4) & 7)) << 3); }
 
-template <int D>
-__global__ __launch_bounds__(kThreads, 2) void prefill_chunk_kernel(PrefillArgs a) {
-    constexpr int KS = D + 8;                   // halfwords per K row in LDS
-    constexpr int DK = D / 16;                  // k-steps of Q.K^T
-    constexpr int NT = D / 32;                  // 32-wide d tiles of the output
-    constexpr int KCH = kKeys * (D / 8) / kThreads;   // 16-byte K chunks staged per thread
-    constexpr int VTASKS = 8 * (D / 4);         // (8-key group, 4 dims) pieces of V per tile
-    constexpr float kRescale = 8.0f;            // rescale O only when a row max grows by > 2^8
-    __shared__ __attribute__((aligned(16))) uint16_t s_k[kKeys * KS];
-    __shared__ __attribute__((aligned(16))) uint16_t s_vt[D * kVtStride];   // V^T as fp16
-
-    // ---- work item: XCD-major so that one (sequence, head) stays on one XCD
-    const int per_xcd = (a.total + kXcds - 1) / kXcds;
-    const int w_idx = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-    if (w_idx >= a.total) return;
-    const int mt = w_idx % a.m_tiles;
-    const int g = (w_idx / a.m_tiles) % a.num_kv_heads;
-    const int s = w_idx / (a.m_tiles * a.num_kv_heads);
-    const int G = a.group;
-    const int q0 = a.cu_q_lens[s];
-    const int C = a.cu_q_lens[s + 1] - q0;
-    const int L = min(a.seq_lens[s], a.max_blocks * kBlk);
-    const int nrows = C * G;
-    const int r0 = mt * kRows;
-    if (r0 >= nrows || C <= 0 || C > L) return;
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int h = lane >> 5;                    // lane half
-    const int base_pos = L - C;                 // position of chunk token 0
-    const int p_min = base_pos + r0 / G;
-    const int p_max = base_pos + (min(nrows, r0 + kRows) - 1) / G;
-
-    // ---- this lane's query row and its Q fragment (B operand of S^T = K Q^T)
-    const int row = r0 + wave * 32 + (lane & 31);
-    const bool row_ok = row < nrows;
-    const int tok = row_ok ? row / G : 0;
-    const int jh = row_ok ? row - tok * G : 0;
-    const int p_row = row_ok ? base_pos + tok : p_max;
-    bf16x8_t qf[DK];
-    {
-        const uint16_t* qp = a.q + ((int64_t)(q0 + tok) * a.num_q_heads + g * G + jh) * D + 8 * h;
-#pragma unroll
-        for (int ks = 0; ks < DK; ++ks) {
-            u32x4_t v = {0u, 0u, 0u, 0u};
-            if (row_ok) v = *reinterpret_cast<const u32x4_t*>(qp + 16 * ks);
-            qf[ks] = as_bf16x8(v);
-        }
-    }
-
-    f32x16_t o[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) o[nt][v] = 0.0f;
-    float m_used = -INFINITY;    // max the weights are taken against (log2 units)
-    float l_run = 0.0f;          // this lane's share of the row sum
-
-    const int k_lo = (a.window > 0) ? max(0, p_min - a.window + 1) : 0;
-    const int kt_first = (k_lo / kKeys) * kKeys;
-    const int last_blk = (L - 1) / kBlk;        // last logical block with keys
-    const int32_t* table = a.block_tables + (int64_t)s * a.max_blocks;
-    const int64_t head_stride = (int64_t)kBlk * D;          // elements per (block, head) tile
-    const int64_t blk_stride = (int64_t)a.num_kv_heads * head_stride;
-
-    // ---- staging roles (every thread): KCH 16-byte K chunks and one V piece
-    //  K chunk c = tid + 256 i: key c / (D/8), dims (c % (D/8)) * 8 .. +8
-    //  V piece t = tid: dims 4 * (t % (D/4)) .. +4 of keys 8 * (t / (D/4)) .. +8
-    const bool v_task = tid < VTASKS;
-    const int v_dq = tid % (D / 4);
-    const int v_kg = tid / (D / 4);
-    u32x4_t kreg[KCH];
-    u32x2_t vreg[8];
-    int id0 = 0, id1 = 0, id2 = 0, id3 = 0;     // physical blocks of the tile (0 when invalid)
-    int vmask = 0;                              // bit b: block b of the tile holds keys
-
-    // The tile's block ids are wave-uniform: read once, before any K/V load,
-    // so the 12 loads of a tile issue back to back.
-    auto tile_ids = [&](int kt) {
-        int m = 0;
-        int got[4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int lb = kt / kBlk + b;
-            const int id = lb <= last_blk ? table[lb] : -1;
-            const bool ok = id >= 0 && id < a.num_blocks;
-            got[b] = ok ? id : 0;               // an invalid block reads block 0 and is masked
-            m |= (ok ? 1 : 0) << b;
-        }
-        id0 = got[0]; id1 = got[1]; id2 = got[2]; id3 = got[3];
-        return m;
-    };
-    auto sel = [&](int b) { return b == 0 ? id0 : (b == 1 ? id1 : (b == 2 ? id2 : id3)); };
-    // Each thread's pieces of a tile lie in fixed blocks of the tile: K chunk i
-    // in block (KCH_BLK i + lane-dependent part), the V piece in block
-    // (8 v_kg) / 16.  The block ids are wave-uniform (scalar registers), so
-    // an address is a scalar base plus a 32-bit per-thread offset.
-    const int k_off = ((tid / (D / 8)) % kBlk) * D + (tid % (D / 8)) * 8;     // within the block's head tile
-    const int v_off = ((8 * v_kg) % kBlk) * D + 4 * v_dq;
-    auto blk_base = [&](const uint16_t* pool, int id) { return pool + (int64_t)id * blk_stride + g * head_stride; };
-    auto load_tile = [&]() {
-#pragma unroll
-        for (int i = 0; i < KCH; ++i) {
-            // chunk i of this thread is key (tid + 256 i) / (D / 8), in block
-            // (256 i + tid) / KPB = b_lo + tid / KPB
-            constexpr int KPB = kBlk * (D / 8);                 // chunks per block
-            static_assert(kThreads % KPB == 0, "K chunks of a thread stay block-aligned");
-            const int b_lo = (kThreads * i) / KPB;
-            const int id = kThreads == KPB ? sel(b_lo) : sel(b_lo + tid / KPB);
-            kreg[i] = *reinterpret_cast<const u32x4_t*>(blk_base(a.k_pool, id) + k_off);
-        }
-        if (v_task) {
-            // block of the V piece: (8 v_kg) / 16 = tid / (2 (D / 4))
-            constexpr int TPB = 2 * (D / 4);                    // V threads per block
-            const int id = sel(tid / TPB);
-            const uint16_t* vp = blk_base(a.v_pool, id) + v_off;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) vreg[i] = *reinterpret_cast<const u32x2_t*>(vp + i * D);
-        }
-    };
-    auto store_tile = [&](int kt, int m) {
-#pragma unroll
-        for (int i = 0; i < KCH; ++i) {
-            const int c = tid + kThreads * i;
-            const int key = c / (D / 8), dc = c % (D / 8);
-            *reinterpret_cast<u32x4_t*>(&s_k[swap23(key) * KS + dc * 8]) = kreg[i];
-        }
-        if (v_task) {
-            // zero keys of invalid blocks and unwritten tail slots (>= L): they may hold NaN
-            uint32_t w[8][2];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                w[i][0] = vreg[i][0];
-                w[i][1] = vreg[i][1];
-            }
-            if (m != 15 || kt + kKeys > L) {    // edge tile (uniform branch)
-                const bool blk_live = (m >> ((8 * v_kg) / kBlk)) & 1;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const bool live = blk_live && kt + 8 * v_kg + i < L;
-                    w[i][0] = live ? w[i][0] : 0u;
-                    w[i][1] = live ? w[i][1] : 0u;
-                }
-            }
-            // 8 keys x 4 dims -> 4 rows of 8 keys, bf16 -> fp16
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int word = e >> 1;
-                u32x4_t r;
-#pragma unroll
-                for (int mm = 0; mm < 4; ++mm) {
-                    const uint32_t a0 = w[2 * mm][word], a1 = w[2 * mm + 1][word];
-                    r[mm] = (e & 1) ? pack_f16x2(bf16hi(a0), bf16hi(a1)) : pack_f16x2(bf16lo(a0), bf16lo(a1));
-                }
-                const int d = 4 * v_dq + e;
-                *reinterpret_cast<u32x4_t*>(&s_vt[d * kVtStride + vt_col(d, v_kg)]) = r;
-            }
-        }
-    };
-
-    if (kt_first <= p_max) {
-        vmask = tile_ids(kt_first);
-        load_tile();
-    }
-    for (int kt = kt_first; kt <= p_max; kt += kKeys) {
-        __syncthreads();                        // every wave is done with the previous tile
-        const int tmask = vmask;
-        store_tile(kt, tmask);
-        __syncthreads();
-        if (kt + kKeys <= p_max) {              // prefetch the next tile while this one is used
-            vmask = tile_ids(kt + kKeys);
-            load_tile();
-        }
-
-        // ---- S^T = K Q^T for the wave's 32 rows: two 32-key halves, their MFMA
-        // chains interleaved (independent accumulators) and the next k-step's
-        // K operands read from LDS before the current k-step's MFMAs issue
-        f32x16_t sacc[2];
-#pragma unroll
-        for (int T = 0; T < 2; ++T)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) sacc[T][v] = 0.0f;
-        {
-            const uint16_t* kr0 = &s_k[(lane & 31) * KS + 8 * h];
-            const uint16_t* kr1 = kr0 + 32 * KS;
-            u32x4_t k0 = *reinterpret_cast<const u32x4_t*>(kr0);
-            u32x4_t k1 = *reinterpret_cast<const u32x4_t*>(kr1);
-#pragma unroll
-            for (int ks = 0; ks < DK; ++ks) {
-                u32x4_t n0 = k0, n1 = k1;
-                if (ks + 1 < DK) {
-                    n0 = *reinterpret_cast<const u32x4_t*>(kr0 + 16 * (ks + 1));
-                    n1 = *reinterpret_cast<const u32x4_t*>(kr1 + 16 * (ks + 1));
-                }
-                sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k0), qf[ks], sacc[0], 0, 0, 0);
-                sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k1), qf[ks], sacc[1], 0, 0, 0);
-                k0 = n0;
-                k1 = n1;
-            }
-        }
-
-        // ---- masks (edge tiles only): key of accumulator v = kt + 32T + 16(v/8) + 8h + v%8
-        const bool full = tmask == 15 && kt + kKeys - 1 <= p_min && (a.window <= 0 || kt >= p_max - a.window + 1);
-        if (!full) {
-#pragma unroll
-            for (int T = 0; T < 2; ++T)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int key = kt + 32 * T + 16 * (v / 8) + 8 * h + (v % 8);
-                    const bool vis = ((tmask >> ((key - kt) / kBlk)) & 1) && key <= p_row &&
-                                     (a.window <= 0 || key > p_row - a.window);
-                    sacc[T][v] = vis ? sacc[T][v] : -INFINITY;
-                }
-        }
-
-        // ---- online softmax for the row (lane-local + lane^32), lazy rescale
-        float mt_ = -INFINITY;
-#pragma unroll
-        for (int T = 0; T < 2; ++T)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) mt_ = fmaxf(mt_, sacc[T][v]);
-        mt_ = fmaxf(mt_, __shfl_xor(mt_, 32, kWave));
-        const float m_tile = mt_ == -INFINITY ? -INFINITY : mt_ * a.scale_log2;
-        const bool grow = m_tile > m_used + kRescale || (m_used == -INFINITY && m_tile != -INFINITY);
-        if (__builtin_amdgcn_ballot_w64(grow)) {
-            const float m_new = grow ? m_tile : m_used;
-            const float alpha = (m_used == -INFINITY) ? 0.0f : fast_exp2(m_used - m_new);
-            m_used = m_new;
-            l_run *= grow ? alpha : 1.0f;
-            const float f = grow ? alpha : 1.0f;
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) o[nt][v] *= f;
-        }
-        const float msub = (m_used == -INFINITY) ? 0.0f : m_used;
-        uint32_t pw[2][8];                       // P^T as fp16 pairs: [T][4u + word]
-        if (a.scale_log2 > 0.0f) {
-            // a masked score (-inf) scales to -inf and exp2 gives 0 by itself
-#pragma unroll
-            for (int T = 0; T < 2; ++T)
-#pragma unroll
-                for (int v = 0; v < 16; v += 2)
-                    pw[T][v / 2] = pack_f16x2(fast_exp2(fmaf(sacc[T][v], a.scale_log2, -msub)),
-                                              fast_exp2(fmaf(sacc[T][v + 1], a.scale_log2, -msub)));
-        } else {
-            // scale 0: -inf * 0 would be NaN, so masked scores are selected away
-#pragma unroll
-            for (int T = 0; T < 2; ++T)
-#pragma unroll
-                for (int v = 0; v < 16; v += 2) {
-                    const float x0 = sacc[T][v], x1 = sacc[T][v + 1];
-                    const float p0 = (x0 == -INFINITY) ? 0.0f : fast_exp2(fmaf(x0, a.scale_log2, -msub));
-                    const float p1 = (x1 == -INFINITY) ? 0.0f : fast_exp2(fmaf(x1, a.scale_log2, -msub));
-                    pw[T][v / 2] = pack_f16x2(p0, p1);
-                }
-        }
-        // row sum of the fp16 weights -- the values P.V multiplies -- two per dot2
-        {
-            const f16x2_t one = {(_Float16)1.0f, (_Float16)1.0f};
-            float ls0 = 0.0f, ls1 = 0.0f;
-#pragma unroll
-            for (int w = 0; w < 8; ++w) {
-                ls0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pw[0][w]), one, ls0, false);
-                ls1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pw[1][w]), one, ls1, false);
-            }
-            l_run += ls0 + ls1;
-        }
-
-        // ---- O^T += V^T P^T: k-step ks covers keys 16ks..16ks+15 (tile T = ks/2, u = ks%2).
-        // Lane reads V^T row d = 32 nt + (lane & 31), key group g = 2 ks + h, at
-        // vt_col(d, g) = 8 * (g ^ ((d >> 4) & 7)) = 16 (ks ^ nt) + 8 (h ^ bit 4 of lane):
-        // one per-lane base plus a compile-time offset per (nt, ks).
-        const uint16_t* vt_base = &s_vt[(lane & 31) * kVtStride + 8 * (h ^ ((lane >> 4) & 1))];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const int T = ks >> 1, u = ks & 1;
-            u32x4_t pb;
-            pb[0] = pw[T][4 * u + 0]; pb[1] = pw[T][4 * u + 1];
-            pb[2] = pw[T][4 * u + 2]; pb[3] = pw[T][4 * u + 3];
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const u32x4_t vv = *reinterpret_cast<const u32x4_t*>(
-                    vt_base + 32 * nt * kVtStride + 16 * ((ks ^ nt) & 7));
-                o[nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(vv), as_f16x8(pb), o[nt], 0, 0, 0);
-            }
-        }
-    }
-
-    // ---- normalise and store: lane holds d = 32nt + 8(v/4) + 4h + v%4 of its row
-    const float l_row = l_run + __shfl_xor(l_run, 32, kWave);
-    if (!row_ok) return;
-    const float inv = l_row > 0.0f ? 1.0f / l_row : 0.0f;
-    const int64_t obase = ((int64_t)(q0 + tok) * a.num_q_heads + g * G + jh) * D;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int v4 = 0; v4 < 4; ++v4) {
-            const int d = 32 * nt + 8 * v4 + 4 * h;
-            const float r0_ = o[nt][4 * v4 + 0] * inv, r1_ = o[nt][4 * v4 + 1] * inv;
-            const float r2_ = o[nt][4 * v4 + 2] * inv, r3_ = o[nt][4 * v4 + 3] * inv;
-            if (a.out_bf16) {
-                u32x2_t pk;
-                pk[0] = pack_bf16x2(r0_, r1_);
-                pk[1] = pack_bf16x2(r2_, r3_);
-                *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(a.out) + obase + d) = pk;
-            } else {
-                f32x4_t fv = {r0_, r1_, r2_, r3_};
-                *reinterpret_cast<f32x4_t*>(static_cast<float*>(a.out) + obase + d) = fv;
-            }
-        }
-}
-
-// ---------------------------------------------------------------------------
-// Pipelined variant: W waves (32 query rows each) share double-buffered K/V
-// tiles, and each wave issues the next tile's S^T = K Q^T MFMAs before this
-// tile's softmax, so the matrix cores work while the VALU computes exp2.
+// W waves (32 query rows each) share double-buffered K/V tiles; each wave
+// issues the next tile's S^T = K Q^T MFMAs with this tile's softmax.
 template <int D, int W, bool ZS>
 __global__ __launch_bounds__(64 * W) void prefill_pipe_kernel(PrefillArgs a) {
     constexpr int NTH = 64 * W;                 // threads
