@@ -84,6 +84,19 @@ def test_sliding_window(window, part):
     assert_close(out, expected_outputs(case), "bf16", f"W={window} P={part}")
 
 
+@pytest.mark.parametrize("dt,kv", [("bf16", "bf16"), ("f32", "f32"), ("bf16", "i8")])
+@pytest.mark.parametrize("window", [0, 5000])
+def test_long_contexts_in_one_pass(dt, kv, window):
+    """partition_size 0: one item walks the whole context, so its block ids come
+    in several batches (4096 keys each); lengths straddle the batch edges and
+    the window starts inside a batch."""
+    lens = [4095, 4096, 4097, 9000, 12345]
+    case = workloads.make_case("long", 78, lens, [1] * len(lens), 8, 2, 128, in_dtype=dt, kv_dtype=kv,
+                               window=window)
+    out, _ = _gpu(case, partition_size=0)
+    assert_close(out, expected_outputs(case), dt, f"{kv} W={window}")
+
+
 def test_empty_context_rows_are_zero():
     case = workloads.make_case("empty", 74, [0, 3, 0, 700], [1] * 4, 8, 2, 128)
     dev = device()
