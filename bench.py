@@ -190,6 +190,9 @@ def bench_decode(args, torch, pkv, workloads, tl):
                          "step_p10": float(np.percentile(t_step, 10)) * 1e3,
                          "step_p90": float(np.percentile(t_step, 90)) * 1e3},
         "bytes": b,
+        # the step's cache write on its own: read and write of the 256 new K/V vectors
+        "kv_cache_write": {"us": round(float(np.mean(t_write)) * 1e3, 2), "bytes": wb,
+                           "GB/s": round(wb / (float(np.mean(t_write)) / 1e3) / 1e9, 1)},
         "roofline": {"kernel": "decode_partition_kernel<bf16, D=128, G=4>", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -197,6 +200,19 @@ def bench_decode(args, torch, pkv, workloads, tl):
                      "algorithmic_bytes_per_launch": part_bytes},
         "max_abs_err": float(err),
     }
+
+
+def host_cpu():
+    """Host CPU model and logical core count (the oracle runs on one of them)."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"model": model, "logical_cores": os.cpu_count()}
 
 
 def cpu_baseline(case, torch, dev):
@@ -214,7 +230,7 @@ def cpu_baseline(case, torch, dev):
     kv = decode_bytes(case)
     step_bytes = sum(kv.values()) + write_bytes(case.num_seqs, case.num_kv_heads, case.head_dim)
     return {"value": round(step_bytes / dt / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "seconds": round(dt, 3),
+            "seconds": round(dt, 3), "host": host_cpu(),
             "sample": f"the whole decode step: all {case.num_seqs} sequences, "
                       f"{int(case.seq_lens.sum())} context tokens, gather + two-pass fp64 attention "
                       f"on one host thread"}
@@ -371,6 +387,7 @@ def main():
         "roofline": d["roofline"],
         "cpu_baseline": cpu,
         "breakdown_us": d["breakdown_us"],
+        "kv_cache_write": d["kv_cache_write"],
         "algorithmic_bytes": d["bytes"],
         "max_abs_err_sampled": d["max_abs_err"],
         "prefill": pre,
