@@ -146,7 +146,10 @@ __global__ __launch_bounds__(64 * W) void prefill_pipe_kernel(PrefillArgs a) {
     const int kt_first = (k_lo / kKeys) * kKeys;
     const int n_tiles = kt_first <= p_max ? (p_max - kt_first) / kKeys + 1 : 0;
     const int last_blk = (L - 1) / kBlk;        // last logical block with keys
-    const int32_t* table = a.block_tables + (int64_t)s * a.max_blocks;
+    // read-only during the kernel: through the constant address space its reads stay
+    // scalar loads whatever else the kernel does
+    const __attribute__((address_space(4))) int32_t* table =
+        (const __attribute__((address_space(4))) int32_t*)(a.block_tables + (int64_t)s * a.max_blocks);
     const int64_t head_stride = (int64_t)kBlk * D;          // elements per (block, head) tile
     const int64_t blk_stride = (int64_t)a.num_kv_heads * head_stride;
 
@@ -350,7 +353,11 @@ __global__ __launch_bounds__(64 * W) void prefill_pipe_kernel(PrefillArgs a) {
         load_tile();
     }
     __syncthreads();                            // tile 0 visible
-    if (n_tiles > 0) compute_s(sa, 0);
+    // unconditional (with no tile it reads stale LDS and the result is unused): Q's
+    // first use is then on every path into the loop, so the wait the compiler puts
+    // on Q's loads stays out of the loop, where it would also cover the tile loads
+    // just issued and expose their latency every tile
+    compute_s(sa, 0);
     if (n_tiles > 1) store_tile(1, kt_of(1), mk1);
     if (n_tiles > 2) {
         mk2 = tile_ids(kt_of(2));
