@@ -65,6 +65,10 @@ def _declare(L):
     L.orc_quantize_vector.argtypes = [P, i32, P, P]
     L.orc_kv_write.restype = ctypes.c_int
     L.orc_kv_write.argtypes = [i32, i32, i32, i32, i32, P, P, i32, i64, P, i32, P, P, P, P]
+    L.orc_slot_mapping.restype = ctypes.c_int
+    L.orc_slot_mapping.argtypes = [i32, i32, i32, P, P, P, i32, P]
+    L.orc_copy_blocks.restype = ctypes.c_int
+    L.orc_copy_blocks.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P, P, i32]
     L.orc_attention.restype = ctypes.c_int
     L.orc_attention.argtypes = [i32, i32, i32, i32, i32, P, i32, i32, i32, P, P, P, P, P, P, P,
                                 i32, f32, i32, P, P, i64]
@@ -166,6 +170,30 @@ class Cache:
                                 slots.size, _ptr(self.k), _ptr(self.v), _ptr(self.k_scale),
                                 _ptr(self.v_scale))
         _check(rc, "kv_write")
+
+
+def slot_mapping(num_blocks, block_size, cu_q_lens, seq_lens, block_tables) -> np.ndarray:
+    """Reference slot of every new row: row i of sequence s sits at position
+    seq_lens[s] - C_s + i; -1 where the table holds no valid block."""
+    cu = _c(cu_q_lens, np.int32)
+    lens = _c(seq_lens, np.int32)
+    tables = _c(block_tables, np.int32)
+    out = np.empty(int(cu[-1]) if cu.size else 0, np.int32)
+    rc = lib().orc_slot_mapping(num_blocks, block_size, lens.size, _ptr(cu), _ptr(lens), _ptr(tables),
+                                tables.shape[1] if tables.ndim == 2 else 0, _ptr(out))
+    _check(rc, "slot_mapping")
+    return out
+
+
+def copy_blocks(cache: "Cache", src, dst) -> None:
+    """Reference block copy: block dst[n] of every pool becomes block src[n]."""
+    src = _c(src, np.int32)
+    dst = _c(dst, np.int32)
+    if src.shape != dst.shape:
+        raise ValueError("src and dst differ in length")
+    rc = lib().orc_copy_blocks(*cache.desc(), _ptr(cache.k), _ptr(cache.v), _ptr(cache.k_scale),
+                               _ptr(cache.v_scale), _ptr(src), _ptr(dst), src.size)
+    _check(rc, "copy_blocks")
 
 
 def attention(cache: Cache, q, q_dtype, cu_q_lens, seq_lens, block_tables, softmax_scale,

@@ -217,6 +217,89 @@ int orc_kv_write(int32_t num_blocks, int32_t block_size, int32_t num_kv_heads, i
     return 0;
 }
 
+/* ------------------------------------------------------------ slot mapping */
+
+/*
+ * Slot of every new row of a step ("MicroGen", Key Features: logical blocks
+ * map to physical blocks through the sequence's table; "PyTorch LLM Serving
+ * Engine", Loading: the new K/V go to a physical cache slot).  Sequence s owns
+ * rows [cu_q_lens[s], cu_q_lens[s+1]), C_s of them, and holds L_s = seq_lens[s]
+ * tokens once they are written, so its row i sits at position p = L_s - C_s + i
+ * and goes to
+ *     slot = block_tables[s][p / block_size] * block_size + p % block_size.
+ * A row whose position is negative or past the table, or whose table entry is
+ * not a block of the pool, gets -1 (the cache write skips it).
+ */
+int orc_slot_mapping(int32_t num_blocks, int32_t block_size, int32_t num_seqs,
+                     const int32_t* cu_q_lens, const int32_t* seq_lens,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t* slots)
+{
+    if (block_size <= 0 || num_seqs < 0 || max_blocks_per_seq < 0) return 1;
+    for (int32_t s = 0; s < num_seqs; ++s) {
+        int32_t r0 = cu_q_lens[s], r1 = cu_q_lens[s + 1];
+        for (int32_t r = r0; r < r1; ++r) {
+            int64_t p = (int64_t)seq_lens[s] - (r1 - r0) + (r - r0);
+            int32_t slot = -1;
+            if (p >= 0 && p / block_size < max_blocks_per_seq) {
+                int32_t blk = block_tables[(int64_t)s * max_blocks_per_seq + p / block_size];
+                if (blk >= 0 && blk < num_blocks)
+                    slot = (int32_t)((int64_t)blk * block_size + p % block_size);
+            }
+            slots[r] = slot;
+        }
+    }
+    return 0;
+}
+
+/*
+ * Copy whole physical blocks: for each pair n, block dst[n] of the K pool, the
+ * V pool and (INT8) both scale pools becomes a copy of block src[n] -- every
+ * KV head and every slot.  This is what sharing a block between sequences
+ * needs before one of them writes into it.  All copies read the pools as they
+ * were before the call (a block copied into is not a source of another pair);
+ * pairs with an id outside [0, num_blocks) are skipped.
+ */
+int orc_copy_blocks(int32_t num_blocks, int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t kv_dtype, void* k_pool, void* v_pool, uint16_t* k_scale,
+                    uint16_t* v_scale, const int32_t* src, const int32_t* dst, int32_t num_pairs)
+{
+    const int esz = elem_size(kv_dtype);
+    if (esz == 0 || num_pairs < 0) return 1;
+    if (kv_dtype == ORC_I8 && (!k_scale || !v_scale)) return 1;
+    const size_t blk_bytes = (size_t)num_kv_heads * block_size * head_dim * esz;
+    const size_t sc_bytes = (size_t)num_kv_heads * block_size * sizeof(uint16_t);
+    char* snap = (char*)malloc(2 * (blk_bytes + sc_bytes) * (size_t)(num_pairs > 0 ? num_pairs : 1));
+    if (!snap) return 2;
+    /* read every source first, then write every destination */
+    for (int pass = 0; pass < 2; ++pass) {
+        for (int32_t n = 0; n < num_pairs; ++n) {
+            if (src[n] < 0 || src[n] >= num_blocks || dst[n] < 0 || dst[n] >= num_blocks) continue;
+            char* keep = snap + (size_t)n * 2 * (blk_bytes + sc_bytes);
+            char* kp = (char*)k_pool;
+            char* vp = (char*)v_pool;
+            if (pass == 0) {
+                memcpy(keep, kp + (size_t)src[n] * blk_bytes, blk_bytes);
+                memcpy(keep + blk_bytes, vp + (size_t)src[n] * blk_bytes, blk_bytes);
+                if (kv_dtype == ORC_I8) {
+                    memcpy(keep + 2 * blk_bytes, (char*)k_scale + (size_t)src[n] * sc_bytes, sc_bytes);
+                    memcpy(keep + 2 * blk_bytes + sc_bytes, (char*)v_scale + (size_t)src[n] * sc_bytes,
+                           sc_bytes);
+                }
+            } else {
+                memcpy(kp + (size_t)dst[n] * blk_bytes, keep, blk_bytes);
+                memcpy(vp + (size_t)dst[n] * blk_bytes, keep + blk_bytes, blk_bytes);
+                if (kv_dtype == ORC_I8) {
+                    memcpy((char*)k_scale + (size_t)dst[n] * sc_bytes, keep + 2 * blk_bytes, sc_bytes);
+                    memcpy((char*)v_scale + (size_t)dst[n] * sc_bytes, keep + 2 * blk_bytes + sc_bytes,
+                           sc_bytes);
+                }
+            }
+        }
+    }
+    free(snap);
+    return 0;
+}
+
 /* ------------------------------------------------------------------ gather */
 
 static double pool_value(const void* pool, const uint16_t* scale, int32_t kv_dtype,

@@ -23,6 +23,14 @@ int orc_kv_write(int32_t num_blocks, int32_t block_size, int32_t num_kv_heads, i
                  int64_t token_stride, const int32_t* slot_mapping, int32_t num_tokens,
                  void* k_pool, void* v_pool, uint16_t* k_scale, uint16_t* v_scale);
 
+int orc_slot_mapping(int32_t num_blocks, int32_t block_size, int32_t num_seqs,
+                     const int32_t* cu_q_lens, const int32_t* seq_lens,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t* slots);
+
+int orc_copy_blocks(int32_t num_blocks, int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t kv_dtype, void* k_pool, void* v_pool, uint16_t* k_scale,
+                    uint16_t* v_scale, const int32_t* src, const int32_t* dst, int32_t num_pairs);
+
 int orc_attention(int32_t num_blocks, int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
                   int32_t kv_dtype, const void* q, int32_t q_dtype, int32_t num_seqs,
                   int32_t num_q_heads, const int32_t* cu_q_lens, const int32_t* seq_lens,

@@ -14,6 +14,7 @@ import pytest
 
 import oracle
 import test_oracle_attention as A
+import test_oracle_blocks as BL
 import test_oracle_int8 as Q
 import test_oracle_numbers as N
 import test_oracle_prefill as P
@@ -50,6 +51,16 @@ MUTANTS = [
      [lambda: P.test_whole_sequence_chunk_equals_causal_sdpa("bf16")]),
     ("merge weights dropped", "double wk = exp(mk - M);", "double wk = 1.0;",
      [lambda: A.test_split_partitions_merge_to_the_two_pass_result(64, 0)]),
+    ("slot one position late", "int64_t p = (int64_t)seq_lens[s] - (r1 - r0) + (r - r0);",
+     "int64_t p = (int64_t)seq_lens[s] - (r1 - r0) + (r - r0) + 1;",
+     [BL.test_slot_mapping_round_trip_equals_dense_causal_attention,
+      BL.test_slot_mapping_identity_table_is_base_plus_position]),
+    ("slot offset in block dropped", "slot = (int32_t)((int64_t)blk * block_size + p % block_size);",
+     "slot = (int32_t)((int64_t)blk * block_size);",
+     [BL.test_slot_mapping_round_trip_equals_dense_causal_attention]),
+    ("block copy reads its own writes", "for (int pass = 0; pass < 2; ++pass) {\n        for (int32_t n = 0; n < num_pairs; ++n) {",
+     "for (int32_t n = 0; n < num_pairs; ++n) {\n        for (int pass = 0; pass < 2; ++pass) {",
+     [lambda: BL.test_copy_blocks_equals_numpy_copy("bf16")]),
 ]
 
 
