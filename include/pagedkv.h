@@ -19,7 +19,8 @@
  *     are passed by value.  `stream` is a hipStream_t (NULL: the null stream).
  *   - Calls only enqueue work on `stream`; they never synchronise.  The caller
  *     owns every buffer and keeps it alive until that work has completed.
- *   - The library allocates no device memory and keeps no per-call state.
+ *   - The library allocates no device memory and keeps no per-call state (the
+ *     block allocator below is host state the caller creates and owns).
  *   - Return value: PKV_OK (0) or a pkv_status.  Host-visible arguments are
  *     validated before anything is enqueued; on failure nothing is enqueued
  *     and pkv_last_error() describes the problem.  No exception crosses the ABI.
@@ -61,7 +62,8 @@ typedef enum {
     PKV_EINVAL = 1,       /* an argument is malformed (null pointer, negative size, ...) */
     PKV_EUNSUPPORTED = 2, /* well-formed but not implemented (dtype pair, head_dim, block_size) */
     PKV_EWORKSPACE = 3,   /* workspace missing or smaller than the query function's answer */
-    PKV_EHIP = 4          /* the HIP runtime reported an error (text in pkv_last_error) */
+    PKV_EHIP = 4,         /* the HIP runtime reported an error (text in pkv_last_error) */
+    PKV_ENOSPACE = 5      /* the block allocator has too few free blocks (nothing was changed) */
 } pkv_status;
 
 /* Shape and element type of one layer's cache. */
@@ -128,7 +130,9 @@ size_t paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_q_hea
  *   out           [num_seqs][num_q_heads][head_dim] of out_dtype (F32 or BF16).
  *   k_scale/v_scale  INT8 pools only, else NULL.
  *   block_tables  [num_seqs][max_blocks_per_seq] int32 physical block ids;
- *                 entries past ceil(L / block_size) are never read.
+ *                 entries past ceil(L / block_size) are never read, and with a
+ *                 window neither are entries wholly before it (they may be -1
+ *                 after pkv_seq_evict_window).
  *   context_lens  [num_seqs] int32.
  *   partition_size  0: each sequence in one pass.  Otherwise a positive
  *                 multiple of block_size: contexts are split into partitions
@@ -174,6 +178,9 @@ int paged_attention_decode(const pkv_cache_desc* cache,
  *   max_q_len     host-side upper bound of every C_s (sizes the grid); rows of
  *                 a longer chunk beyond max_q_len are not computed.
  *   seq_lens      [num_seqs] int32, L_s >= C_s.
+ *   block_tables  as for decode; with a window, entries wholly before the
+ *                 first row's window may be -1 (evicted): they hold no key
+ *                 any row can see.
  * Pools must be BF16.  num_seqs == 0 or max_q_len == 0 is a no-op.
  */
 int paged_attention_prefill_chunk(const pkv_cache_desc* cache,
@@ -186,6 +193,126 @@ int paged_attention_prefill_chunk(const pkv_cache_desc* cache,
                                   const int32_t* seq_lens,
                                   float softmax_scale, int32_t sliding_window,
                                   void* stream);
+
+/*
+ * pkv_build_slot_mapping -- the cache slot of every new row of a step, on the
+ * device, from the block tables.
+ * ("MicroGen", Key Features: logical blocks map to physical blocks through the
+ * sequence's table; "PyTorch LLM Serving Engine", Loading: each new K/V vector
+ * goes to a physical cache slot.)
+ *
+ * Sequence s owns rows [cu_q_lens[s], cu_q_lens[s+1]) (C_s of them: 1 for a
+ * decode step, the chunk length for prefill) and holds L_s = seq_lens[s]
+ * tokens once they are written, so row i sits at position p = L_s - C_s + i:
+ *     slot_mapping[row] = block_tables[s][p / block_size] * block_size + p % block_size
+ * or -1 (kv_cache_write then skips the row) when p < 0, p / block_size >=
+ * max_blocks_per_seq, or the table entry is outside [0, num_blocks).
+ *
+ *   cu_q_lens     [num_seqs + 1] int32 prefix sums, cu_q_lens[0] == 0.
+ *   seq_lens      [num_seqs] int32.
+ *   block_tables  [num_seqs][max_blocks_per_seq] int32.
+ *   slot_mapping  [total_rows] int32 output; rows at or past total_rows are
+ *                 not written (total_rows is the array's length, normally
+ *                 cu_q_lens[num_seqs]).
+ * Only cache->num_blocks and cache->block_size are used.  num_seqs == 0 or
+ * total_rows == 0 is a no-op.
+ */
+int pkv_build_slot_mapping(const pkv_cache_desc* cache, const int32_t* cu_q_lens, int32_t num_seqs,
+                           const int32_t* seq_lens, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           int32_t* slot_mapping, int32_t total_rows, void* stream);
+
+/*
+ * kv_cache_copy_blocks -- copy whole physical blocks: for each pair n, block
+ * dst_blocks[n] of the K pool, the V pool and (INT8) both scale pools becomes
+ * a copy of block src_blocks[n], every KV head and slot.  A sequence that
+ * shares a partly filled block with another (a forked prefix, "MicroGen", Key
+ * Features) copies it before writing into it; pkv_seq_append names the pairs.
+ *
+ *   src_blocks, dst_blocks  [num_pairs] int32 device arrays.  A pair naming a
+ *                 block outside [0, num_blocks) is skipped.  Destinations must
+ *                 be distinct and no destination may be the source of another
+ *                 pair (otherwise the result is unspecified).
+ *   k_scale/v_scale  INT8 pools only (4-byte aligned), else NULL.
+ * num_pairs == 0 is a no-op.
+ */
+int kv_cache_copy_blocks(const pkv_cache_desc* cache, void* k_pool, void* v_pool, void* k_scale, void* v_scale,
+                         const int32_t* src_blocks, const int32_t* dst_blocks, int32_t num_pairs, void* stream);
+
+/*
+ * Block allocator -- host-side owner of a pool's physical blocks ("PyTorch LLM
+ * Serving Engine", What is implemented: fixed-size physical blocks handed out
+ * through per-sequence block tables).  Free blocks are kept on a stack (O(1)
+ * per block); every block carries a reference count so that sequences can
+ * share blocks (a forked prefix) and a block is free again when its count
+ * drops to zero.  The allocator touches no device memory: table rows are HOST
+ * int32 arrays the caller owns and copies to the device for the kernels.
+ * Entries that hold no block are -1.  Every call validates first and changes
+ * nothing on failure.  One allocator must not be used by two threads at once.
+ */
+typedef struct pkv_block_allocator pkv_block_allocator;
+
+/* New allocator for blocks 0 .. num_blocks-1, all free; *out is NULL on failure. */
+int pkv_allocator_create(int32_t num_blocks, int32_t block_size, pkv_block_allocator** out);
+/* Free the allocator (NULL is allowed). */
+int pkv_allocator_destroy(pkv_block_allocator* a);
+/* Number of free blocks (-1 for NULL). */
+int32_t pkv_allocator_num_free(const pkv_block_allocator* a);
+/* References held on `block` (0 = free; -1 for an id outside the pool). */
+int32_t pkv_allocator_refcount(const pkv_block_allocator* a, int32_t block);
+/* Take n free blocks into ids[0..n) (count 1 each); PKV_ENOSPACE if fewer are free. */
+int pkv_allocator_alloc(pkv_block_allocator* a, int32_t n, int32_t* ids);
+/* One more reference on each allocated block of ids (negative ids are skipped). */
+int pkv_allocator_retain(pkv_block_allocator* a, const int32_t* ids, int32_t n);
+/* Drop one reference on each block of ids (negative ids skipped); a block whose
+ * count reaches 0 is free.  Releasing more references than held: PKV_EINVAL. */
+int pkv_allocator_release(pkv_block_allocator* a, const int32_t* ids, int32_t n);
+
+/*
+ * pkv_seq_append -- make room for num_new tokens after the len tokens of a
+ * sequence whose table row is table_row[0 .. max_blocks_per_seq).  Blocks are
+ * allocated for the logical blocks that positions len .. len+num_new-1 start.
+ * If position len falls inside a block that other sequences also hold (count
+ * > 1), that entry is replaced by a fresh block and the pair (old, fresh) is
+ * returned in copy_src[0], copy_dst[0] with *num_copies = 1 (else 0): the
+ * caller copies it with kv_cache_copy_blocks before the cache write.  The slot
+ * of each new token then follows from the table (pkv_build_slot_mapping).
+ * copy_src and copy_dst hold at least one entry.  PKV_ENOSPACE if the pool
+ * cannot supply every block needed.
+ */
+int pkv_seq_append(pkv_block_allocator* a, int32_t* table_row, int32_t max_blocks_per_seq, int32_t len,
+                   int32_t num_new, int32_t* copy_src, int32_t* copy_dst, int32_t* num_copies);
+
+/*
+ * pkv_seq_fork -- a new sequence that shares the first len tokens of a parent
+ * (prefix reuse, "MicroGen", Key Features): child_row receives the parent's
+ * ceil(len / block_size) entries, each block gains a reference, and the rest
+ * of child_row[0 .. max_blocks_per_seq) is set to -1.  No bytes are copied;
+ * the attention kernels read shared blocks like private ones.
+ */
+int pkv_seq_fork(pkv_block_allocator* a, const int32_t* parent_row, int32_t len, int32_t* child_row,
+                 int32_t max_blocks_per_seq);
+
+/*
+ * pkv_seq_truncate -- roll a sequence back from len to new_len tokens (rejected
+ * draft tokens of speculative decoding, "MicroGen", Key Features): entries
+ * from ceil(new_len / block_size) to ceil(len / block_size) are released and
+ * set to -1.  Positions >= new_len inside the kept last block are simply
+ * overwritten by the next append.  Also frees a whole sequence (new_len 0).
+ */
+int pkv_seq_truncate(pkv_block_allocator* a, int32_t* table_row, int32_t len, int32_t new_len);
+
+/*
+ * pkv_seq_evict_window -- window-length eviction ("MicroGen", Key Features):
+ * once a sequence holds len tokens, every later query sits at position >= len
+ * and, with sliding window W, sees only keys j > len - W.  The blocks wholly
+ * before that, entries 0 .. floor((len - W + 1) / block_size) - 1, are
+ * released and set to -1; *num_released (may be NULL) counts the entries
+ * released by this call.  The attention calls never read an entry before the
+ * window, and treat an entry of -1 as no keys, so their results are unchanged
+ * as long as they run with the same window.
+ */
+int pkv_seq_evict_window(pkv_block_allocator* a, int32_t* table_row, int32_t len, int32_t window,
+                         int32_t* num_released);
 
 /* Text for the last non-OK status returned on this thread ("" if none). */
 const char* pkv_last_error(void);

@@ -18,12 +18,17 @@ LIB_PATH = os.path.join(PKG, "libpagedkv.so")
 
 PKV_F32, PKV_BF16, PKV_I8 = 1, 2, 4
 _TORCH_TO_PKV = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16, torch.int8: PKV_I8}
-STATUS = {0: "PKV_OK", 1: "PKV_EINVAL", 2: "PKV_EUNSUPPORTED", 3: "PKV_EWORKSPACE", 4: "PKV_EHIP"}
+STATUS = {0: "PKV_OK", 1: "PKV_EINVAL", 2: "PKV_EUNSUPPORTED", 3: "PKV_EWORKSPACE", 4: "PKV_EHIP",
+          5: "PKV_ENOSPACE"}
 
 # every symbol include/pagedkv.h declares
 EXPORTS = ("kv_cache_write", "paged_attention_decode_workspace_size", "paged_attention_decode",
            "paged_attention_prefill_chunk", "pkv_last_error", "pkv_version",
-           "pkv_profile_set_decode_split_event", "pkv_profile_set_decode_start_event")
+           "pkv_profile_set_decode_split_event", "pkv_profile_set_decode_start_event",
+           "pkv_build_slot_mapping", "kv_cache_copy_blocks", "pkv_allocator_create", "pkv_allocator_destroy",
+           "pkv_allocator_num_free", "pkv_allocator_refcount", "pkv_allocator_alloc", "pkv_allocator_retain",
+           "pkv_allocator_release", "pkv_seq_append", "pkv_seq_fork", "pkv_seq_truncate",
+           "pkv_seq_evict_window")
 
 
 class PagedKVError(RuntimeError):
@@ -71,6 +76,32 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.pkv_profile_set_decode_split_event.argtypes = [P]
             lib.pkv_profile_set_decode_start_event.restype = ctypes.c_int
             lib.pkv_profile_set_decode_start_event.argtypes = [P]
+            lib.pkv_build_slot_mapping.restype = ctypes.c_int
+            lib.pkv_build_slot_mapping.argtypes = [D, P, i32, P, P, i32, P, i32, P]
+            lib.kv_cache_copy_blocks.restype = ctypes.c_int
+            lib.kv_cache_copy_blocks.argtypes = [D, P, P, P, P, P, P, i32, P]
+            lib.pkv_allocator_create.restype = ctypes.c_int
+            lib.pkv_allocator_create.argtypes = [i32, i32, ctypes.POINTER(P)]
+            lib.pkv_allocator_destroy.restype = ctypes.c_int
+            lib.pkv_allocator_destroy.argtypes = [P]
+            lib.pkv_allocator_num_free.restype = i32
+            lib.pkv_allocator_num_free.argtypes = [P]
+            lib.pkv_allocator_refcount.restype = i32
+            lib.pkv_allocator_refcount.argtypes = [P, i32]
+            for name in ("pkv_allocator_alloc",):
+                getattr(lib, name).restype = ctypes.c_int
+                getattr(lib, name).argtypes = [P, i32, P]
+            for name in ("pkv_allocator_retain", "pkv_allocator_release"):
+                getattr(lib, name).restype = ctypes.c_int
+                getattr(lib, name).argtypes = [P, P, i32]
+            lib.pkv_seq_append.restype = ctypes.c_int
+            lib.pkv_seq_append.argtypes = [P, P, i32, i32, i32, P, P, P]
+            lib.pkv_seq_fork.restype = ctypes.c_int
+            lib.pkv_seq_fork.argtypes = [P, P, i32, P, i32]
+            lib.pkv_seq_truncate.restype = ctypes.c_int
+            lib.pkv_seq_truncate.argtypes = [P, P, i32, i32]
+            lib.pkv_seq_evict_window.restype = ctypes.c_int
+            lib.pkv_seq_evict_window.argtypes = [P, P, i32, i32, P]
             _lib = lib
     return _lib
 
@@ -233,6 +264,136 @@ def paged_attention_prefill_chunk(q: torch.Tensor, cu_q_lens: torch.Tensor, seq_
         int(max_q_len), q.shape[1], _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
         max(block_tables.shape[1], 1), _ptr(seq_lens), float(softmax_scale), int(sliding_window), _stream(dev)))
     return out
+
+
+def build_slot_mapping(cu_q_lens: torch.Tensor, seq_lens: torch.Tensor, block_tables: torch.Tensor,
+                       k_pool: torch.Tensor, out: torch.Tensor | None = None,
+                       total_rows: int | None = None) -> torch.Tensor:
+    """Slot of every new row (row i of sequence s at position seq_lens[s] - C_s + i),
+    computed on the GPU from the block tables; -1 where the table holds no block."""
+    dev = _on_gpu(cu_q_lens, seq_lens, block_tables, out)
+    desc = cache_desc(k_pool)
+    b = seq_lens.shape[0]
+    for t, n in ((cu_q_lens, "cu_q_lens"), (seq_lens, "seq_lens"), (block_tables, "block_tables")):
+        if t.dtype != torch.int32:
+            raise ValueError(f"{n} must be int32")
+        _contig(t, n)
+    if cu_q_lens.shape != (b + 1,) or block_tables.dim() != 2 or block_tables.shape[0] != b:
+        raise ValueError("cu_q_lens must be [num_seqs + 1] and block_tables [num_seqs][max_blocks]")
+    if out is None:
+        if total_rows is None:
+            total_rows = int(cu_q_lens[-1].item()) if b else 0
+        out = torch.empty(total_rows, dtype=torch.int32, device=dev)
+    if out.dtype != torch.int32 or out.dim() != 1:
+        raise ValueError("out must be int32 [total_rows]")
+    _contig(out, "out")
+    lib = load_library()
+    _check(lib.pkv_build_slot_mapping(ctypes.byref(desc), _ptr(cu_q_lens), b, _ptr(seq_lens), _ptr(block_tables),
+                                      max(block_tables.shape[1], 1), _ptr(out), out.shape[0], _stream(dev)))
+    return out
+
+
+def kv_cache_copy_blocks(src_blocks: torch.Tensor, dst_blocks: torch.Tensor, k_pool: torch.Tensor,
+                         v_pool: torch.Tensor, k_scale: torch.Tensor | None = None,
+                         v_scale: torch.Tensor | None = None) -> None:
+    """Block dst_blocks[n] of every pool becomes a copy of block src_blocks[n]."""
+    dev = _on_gpu(src_blocks, dst_blocks, k_pool, v_pool, k_scale, v_scale)
+    _check_pools(k_pool, v_pool, k_scale, v_scale)
+    desc = cache_desc(k_pool)
+    if (src_blocks.dtype != torch.int32 or dst_blocks.dtype != torch.int32 or src_blocks.dim() != 1
+            or src_blocks.shape != dst_blocks.shape):
+        raise ValueError("src_blocks and dst_blocks must be int32 [num_pairs]")
+    _contig(src_blocks, "src_blocks")
+    _contig(dst_blocks, "dst_blocks")
+    lib = load_library()
+    _check(lib.kv_cache_copy_blocks(ctypes.byref(desc), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
+                                    _ptr(src_blocks), _ptr(dst_blocks), src_blocks.shape[0], _stream(dev)))
+
+
+def _np_ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _row(a, what):
+    import numpy as np
+    if not isinstance(a, np.ndarray) or a.dtype != np.int32 or a.ndim != 1 or not a.flags.c_contiguous \
+            or not a.flags.writeable:
+        raise ValueError(f"{what} must be a writeable contiguous numpy int32 vector")
+    return a
+
+
+class BlockAllocator:
+    """Host-side owner of a pool's blocks (include/pagedkv.h, pkv_allocator_*):
+    O(1) free stack, reference counts for shared blocks, and the table edits of
+    appending, forking, rolling back and window eviction.  Table rows are numpy
+    int32 vectors (-1 = no block) that the caller copies to the device."""
+
+    def __init__(self, num_blocks: int, block_size: int = 16):
+        self._lib = load_library()
+        h = ctypes.c_void_p()
+        _check(self._lib.pkv_allocator_create(int(num_blocks), int(block_size), ctypes.byref(h)))
+        self._h = h
+        self.num_blocks, self.block_size = int(num_blocks), int(block_size)
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._lib.pkv_allocator_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    @property
+    def num_free(self) -> int:
+        return int(self._lib.pkv_allocator_num_free(self._h))
+
+    def refcount(self, block: int) -> int:
+        return int(self._lib.pkv_allocator_refcount(self._h, int(block)))
+
+    def alloc(self, n: int):
+        import numpy as np
+        ids = np.empty(max(int(n), 1), np.int32)
+        _check(self._lib.pkv_allocator_alloc(self._h, int(n), _np_ptr(ids)))
+        return ids[:int(n)]
+
+    def retain(self, ids):
+        import numpy as np
+        ids = np.ascontiguousarray(ids, np.int32)
+        _check(self._lib.pkv_allocator_retain(self._h, _np_ptr(ids), ids.size))
+
+    def release(self, ids):
+        import numpy as np
+        ids = np.ascontiguousarray(ids, np.int32)
+        _check(self._lib.pkv_allocator_release(self._h, _np_ptr(ids), ids.size))
+
+    def append(self, row, length: int, num_new: int):
+        """Blocks for num_new tokens after `length`; returns the copy-on-write
+        pairs [(src, dst)] to run through kv_cache_copy_blocks first."""
+        import numpy as np
+        row = _row(row, "row")
+        src = np.zeros(1, np.int32)
+        dst = np.zeros(1, np.int32)
+        n = ctypes.c_int32(0)
+        _check(self._lib.pkv_seq_append(self._h, _np_ptr(row), row.size, int(length), int(num_new),
+                                        _np_ptr(src), _np_ptr(dst), ctypes.byref(n)))
+        return [(int(src[0]), int(dst[0]))] if n.value else []
+
+    def fork(self, parent_row, length: int, child_row):
+        import numpy as np
+        parent_row = np.ascontiguousarray(parent_row, np.int32)
+        child_row = _row(child_row, "child_row")
+        _check(self._lib.pkv_seq_fork(self._h, _np_ptr(parent_row), int(length), _np_ptr(child_row),
+                                      child_row.size))
+
+    def truncate(self, row, length: int, new_length: int):
+        row = _row(row, "row")
+        _check(self._lib.pkv_seq_truncate(self._h, _np_ptr(row), int(length), int(new_length)))
+
+    def evict_window(self, row, length: int, window: int) -> int:
+        row = _row(row, "row")
+        n = ctypes.c_int32(0)
+        _check(self._lib.pkv_seq_evict_window(self._h, _np_ptr(row), int(length), int(window), ctypes.byref(n)))
+        return int(n.value)
 
 
 def set_decode_split_event(event) -> None:

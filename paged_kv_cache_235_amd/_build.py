@@ -21,7 +21,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libpagedkv.so")
 ARCH = "gfx950"
 
-SOURCES = ["pkv_api.cpp", "kv_write.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["pkv_api.cpp", "block_allocator.cpp", "kv_write.hip", "decode.hip", "prefill.hip",
+           "block_ops.hip"]
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 instructions.
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -1,0 +1,106 @@
+// block_ops.hip -- block-table bookkeeping on the device: the slot of every
+// new row of a step, and whole-block copies for blocks shared between
+// sequences.
+//
+// "MicroGen", Key Features: logical blocks map to physical blocks through the
+// sequence's table; "PyTorch LLM Serving Engine", Loading: each new K/V
+// vector is written to a physical cache slot, and What is implemented:
+// per-sequence block tables over fixed-size blocks.
+//
+// Slot mapping: one workgroup per sequence walks its rows (a decode step has
+// one, a prefill chunk hundreds); each row reads one table entry.  Block copy:
+// a (pair, piece) grid moves a block's K and V runs with 16-byte loads and
+// stores; INT8 scale runs are copied by the first piece of each pair.
+#include "pkv_internal.h"
+#include "pkv_device.h"
+
+namespace pkv {
+
+__global__ __launch_bounds__(256) void slot_mapping_kernel(const int32_t* cu_q_lens, const int32_t* seq_lens,
+                                                           const int32_t* block_tables, int32_t max_blocks,
+                                                           int32_t block_size, int32_t num_blocks,
+                                                           int32_t* slots, int32_t total_rows) {
+    const int s = blockIdx.x;
+    const int r0 = cu_q_lens[s];
+    const int r1 = cu_q_lens[s + 1];
+    const int64_t first = (int64_t)seq_lens[s] - (r1 - r0);   // position of row r0
+    for (int r = r0 + (int)threadIdx.x; r < r1; r += blockDim.x) {
+        if (r < 0 || r >= total_rows) continue;
+        const int64_t p = first + (r - r0);
+        int32_t slot = -1;
+        if (p >= 0 && p / block_size < max_blocks) {
+            const int32_t id = block_tables[(int64_t)s * max_blocks + p / block_size];
+            if (id >= 0 && id < num_blocks) slot = (int32_t)((int64_t)id * block_size + p % block_size);
+        }
+        slots[r] = slot;
+    }
+}
+
+struct CopyArgs {
+    char* k_pool;
+    char* v_pool;
+    uint16_t* k_scale;
+    uint16_t* v_scale;
+    const int32_t* src;
+    const int32_t* dst;
+    int64_t blk_chunks;      // 16-byte chunks per block of one pool
+    int32_t scale_words;     // 32-bit words per block of one scale pool (0: no scales)
+    int32_t num_blocks;
+};
+
+__global__ __launch_bounds__(256) void copy_blocks_kernel(CopyArgs a) {
+    const int n = blockIdx.x;
+    const int32_t s = a.src[n];
+    const int32_t d = a.dst[n];
+    if (s < 0 || s >= a.num_blocks || d < 0 || d >= a.num_blocks || s == d) return;
+    const int64_t so = (int64_t)s * a.blk_chunks;
+    const int64_t dof = (int64_t)d * a.blk_chunks;
+    const u32x4_t* ks = reinterpret_cast<const u32x4_t*>(a.k_pool) + so;
+    const u32x4_t* vs = reinterpret_cast<const u32x4_t*>(a.v_pool) + so;
+    u32x4_t* kd = reinterpret_cast<u32x4_t*>(a.k_pool) + dof;
+    u32x4_t* vd = reinterpret_cast<u32x4_t*>(a.v_pool) + dof;
+    for (int64_t c = (int64_t)blockIdx.y * blockDim.x + threadIdx.x; c < a.blk_chunks;
+         c += (int64_t)gridDim.y * blockDim.x) {
+        const u32x4_t kv = ks[c];
+        const u32x4_t vv = vs[c];
+        kd[c] = kv;
+        vd[c] = vv;
+    }
+    if (a.scale_words > 0 && blockIdx.y == 0) {
+        const uint32_t* kss = reinterpret_cast<const uint32_t*>(a.k_scale) + (int64_t)s * a.scale_words;
+        const uint32_t* vss = reinterpret_cast<const uint32_t*>(a.v_scale) + (int64_t)s * a.scale_words;
+        uint32_t* ksd = reinterpret_cast<uint32_t*>(a.k_scale) + (int64_t)d * a.scale_words;
+        uint32_t* vsd = reinterpret_cast<uint32_t*>(a.v_scale) + (int64_t)d * a.scale_words;
+        for (int w = threadIdx.x; w < a.scale_words; w += blockDim.x) {
+            const uint32_t kw = kss[w];
+            const uint32_t vw = vss[w];
+            ksd[w] = kw;
+            vsd[w] = vw;
+        }
+    }
+}
+
+hipError_t launch_slot_mapping(const SlotMappingLaunch& L, hipStream_t stream) {
+    return launch(slot_mapping_kernel, dim3(L.num_seqs), dim3(256), 0, stream, L.cu_q_lens, L.seq_lens,
+                  L.block_tables, L.max_blocks_per_seq, L.block_size, L.num_blocks, L.slot_mapping,
+                  L.total_rows);
+}
+
+hipError_t launch_copy_blocks(const CopyBlocksLaunch& L, hipStream_t stream) {
+    CopyArgs a;
+    a.k_pool = static_cast<char*>(L.k_pool);
+    a.v_pool = static_cast<char*>(L.v_pool);
+    a.k_scale = static_cast<uint16_t*>(L.k_scale);
+    a.v_scale = static_cast<uint16_t*>(L.v_scale);
+    a.src = L.src;
+    a.dst = L.dst;
+    const int64_t blk_bytes = (int64_t)L.num_kv_heads * L.block_size * L.head_dim * L.elem_size;
+    a.blk_chunks = blk_bytes / 16;
+    a.scale_words = L.k_scale ? (int32_t)((int64_t)L.num_kv_heads * L.block_size * 2 / 4) : 0;
+    a.num_blocks = L.num_blocks;
+    // pieces of 4 KiB per workgroup (256 threads x 16 B)
+    const int pieces = (int)std::max<int64_t>(1, (a.blk_chunks + 255) / 256);
+    return launch(copy_blocks_kernel, dim3(L.num_pairs, pieces), dim3(256), 0, stream, a);
+}
+
+}  // namespace pkv

@@ -3,6 +3,7 @@
 // Nothing is enqueued unless every host-visible argument is valid.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -79,8 +80,10 @@ int copy_to_host(std::vector<T>& dst, const T* src, size_t n, hipStream_t stream
 }
 
 // PKV_VALIDATE=1: check device-resident tables and lengths on the host.
+// Entries wholly before the window of the call's first query may be -1 (evicted).
 int validate_tables(const pkv_cache_desc* c, int32_t num_seqs, const int32_t* block_tables,
-                    int32_t max_blocks, const int32_t* lens, const int32_t* cu, hipStream_t stream) {
+                    int32_t max_blocks, const int32_t* lens, const int32_t* cu, int32_t window,
+                    hipStream_t stream) {
     std::vector<int32_t> L, T, CU;
     int rc = copy_to_host(L, lens, (size_t)num_seqs, stream);
     if (rc == PKV_OK) rc = copy_to_host(T, block_tables, (size_t)num_seqs * max_blocks, stream);
@@ -96,7 +99,9 @@ int validate_tables(const pkv_cache_desc* c, int32_t num_seqs, const int32_t* bl
             if (C < 0 || C > L[s]) return fail(PKV_EINVAL, "chunk length %d of sequence %d outside [0, %d]", C, s, L[s]);
         }
         const int32_t used = (L[s] + c->block_size - 1) / c->block_size;
-        for (int32_t b = 0; b < used; ++b) {
+        const int64_t first_query = cu ? (int64_t)L[s] - (CU[s + 1] - CU[s]) : (int64_t)L[s] - 1;
+        const int64_t first_key = window > 0 ? std::max<int64_t>(0, first_query - window + 1) : 0;
+        for (int32_t b = (int32_t)(first_key / c->block_size); b < used; ++b) {
             const int32_t id = T[(size_t)s * max_blocks + b];
             if (id < 0 || id >= c->num_blocks)
                 return fail(PKV_EINVAL, "block_tables[%d][%d] = %d outside [0, %d)", s, b, id, c->num_blocks);
@@ -108,6 +113,18 @@ int validate_tables(const pkv_cache_desc* c, int32_t num_seqs, const int32_t* bl
 }  // namespace
 
 namespace pkv {
+int report(int status, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_error = buf;
+    return status;
+}
+
+void clear_error() { g_error.clear(); }
+
 int device_cu_count() {
     static thread_local int cached_dev = -1;
     static thread_local int cached_cus = 0;
@@ -250,7 +267,8 @@ int paged_attention_decode(const pkv_cache_desc* cache, const void* q, int32_t q
     if (need > 0 && !aligned(workspace, 256)) return fail(PKV_EINVAL, "workspace must be 256-byte aligned");
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (validate_env()) {
-        rc = validate_tables(cache, num_seqs, block_tables, max_blocks_per_seq, context_lens, nullptr, st);
+        rc = validate_tables(cache, num_seqs, block_tables, max_blocks_per_seq, context_lens, nullptr,
+                             sliding_window, st);
         if (rc != PKV_OK) return rc;
     }
     pkv::DecodeLaunch L;
@@ -313,7 +331,8 @@ int paged_attention_prefill_chunk(const pkv_cache_desc* cache, const void* q, in
         return fail(PKV_EINVAL, "q, out and the pools must be 16-byte aligned");
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (validate_env()) {
-        rc = validate_tables(cache, num_seqs, block_tables, max_blocks_per_seq, seq_lens, cu_q_lens, st);
+        rc = validate_tables(cache, num_seqs, block_tables, max_blocks_per_seq, seq_lens, cu_q_lens,
+                             sliding_window, st);
         if (rc != PKV_OK) return rc;
     }
     pkv::PrefillLaunch L;
@@ -337,6 +356,94 @@ int paged_attention_prefill_chunk(const pkv_cache_desc* cache, const void* q, in
     L.window = sliding_window;
     const hipError_t e = pkv::launch_prefill(L, st);
     return e == hipSuccess ? PKV_OK : hip_fail(e, "paged_attention_prefill_chunk launch");
+}
+
+
+int pkv_build_slot_mapping(const pkv_cache_desc* cache, const int32_t* cu_q_lens, int32_t num_seqs,
+                           const int32_t* seq_lens, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           int32_t* slot_mapping, int32_t total_rows, void* stream) {
+    g_error.clear();
+    int rc = check_cache(cache);
+    if (rc != PKV_OK) return rc;
+    if (num_seqs < 0 || total_rows < 0) return fail(PKV_EINVAL, "num_seqs and total_rows must be >= 0");
+    if (max_blocks_per_seq <= 0) return fail(PKV_EINVAL, "max_blocks_per_seq must be > 0");
+    if (num_seqs == 0 || total_rows == 0) return PKV_OK;
+    if (num_seqs > 0x7fffffff / 2) return fail(PKV_EUNSUPPORTED, "num_seqs too large");
+    if (!cu_q_lens || !seq_lens || !block_tables || !slot_mapping) return fail(PKV_EINVAL, "NULL tensor pointer");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (validate_env()) {
+        std::vector<int32_t> CU;
+        rc = copy_to_host(CU, cu_q_lens, (size_t)num_seqs + 1, st);
+        if (rc != PKV_OK) return rc;
+        if (CU[0] != 0) return fail(PKV_EINVAL, "cu_q_lens[0] = %d, expected 0", CU[0]);
+        for (int32_t s = 0; s < num_seqs; ++s)
+            if (CU[s + 1] < CU[s]) return fail(PKV_EINVAL, "cu_q_lens decreases at %d", s);
+        if (CU[num_seqs] > total_rows)
+            return fail(PKV_EINVAL, "cu_q_lens[num_seqs] = %d exceeds total_rows %d", CU[num_seqs], total_rows);
+    }
+    pkv::SlotMappingLaunch L;
+    L.cu_q_lens = cu_q_lens;
+    L.seq_lens = seq_lens;
+    L.block_tables = block_tables;
+    L.num_seqs = num_seqs;
+    L.max_blocks_per_seq = max_blocks_per_seq;
+    L.block_size = cache->block_size;
+    L.num_blocks = cache->num_blocks;
+    L.slot_mapping = slot_mapping;
+    L.total_rows = total_rows;
+    const hipError_t e = pkv::launch_slot_mapping(L, st);
+    return e == hipSuccess ? PKV_OK : hip_fail(e, "pkv_build_slot_mapping launch");
+}
+
+int kv_cache_copy_blocks(const pkv_cache_desc* cache, void* k_pool, void* v_pool, void* k_scale, void* v_scale,
+                         const int32_t* src_blocks, const int32_t* dst_blocks, int32_t num_pairs, void* stream) {
+    g_error.clear();
+    int rc = check_cache(cache);
+    if (rc != PKV_OK) return rc;
+    if (num_pairs < 0) return fail(PKV_EINVAL, "num_pairs must be >= 0 (got %d)", num_pairs);
+    const bool i8 = cache->kv_dtype == PKV_I8;
+    if (i8 && (!k_scale || !v_scale)) return fail(PKV_EINVAL, "INT8 pools need k_scale and v_scale");
+    if (!i8 && (k_scale || v_scale))
+        return fail(PKV_EINVAL, "k_scale/v_scale must be NULL for %s pools", dtype_name(cache->kv_dtype));
+    if (num_pairs == 0) return PKV_OK;
+    if (!k_pool || !v_pool || !src_blocks || !dst_blocks) return fail(PKV_EINVAL, "NULL tensor pointer");
+    if (!aligned(k_pool, 16) || !aligned(v_pool, 16)) return fail(PKV_EINVAL, "the pools must be 16-byte aligned");
+    if (i8 && (!aligned(k_scale, 4) || !aligned(v_scale, 4)))
+        return fail(PKV_EINVAL, "scale pools must be 4-byte aligned");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (validate_env()) {
+        std::vector<int32_t> S, D;
+        rc = copy_to_host(S, src_blocks, (size_t)num_pairs, st);
+        if (rc == PKV_OK) rc = copy_to_host(D, dst_blocks, (size_t)num_pairs, st);
+        if (rc != PKV_OK) return rc;
+        std::vector<char> role((size_t)cache->num_blocks, 0);   // bit 0: source, bit 1: destination
+        for (int32_t n = 0; n < num_pairs; ++n) {
+            if (S[n] < 0 || S[n] >= cache->num_blocks || D[n] < 0 || D[n] >= cache->num_blocks)
+                return fail(PKV_EINVAL, "pair %d (%d -> %d) names a block outside [0, %d)", n, S[n], D[n],
+                            cache->num_blocks);
+            role[S[n]] |= 1;
+        }
+        for (int32_t n = 0; n < num_pairs; ++n) {
+            if (role[D[n]] & 2) return fail(PKV_EINVAL, "block %d is the destination of two pairs", D[n]);
+            if ((role[D[n]] & 1) && S[n] != D[n]) return fail(PKV_EINVAL, "block %d is both a source and a destination", D[n]);
+            role[D[n]] |= 2;
+        }
+    }
+    pkv::CopyBlocksLaunch L;
+    L.k_pool = k_pool;
+    L.v_pool = v_pool;
+    L.k_scale = k_scale;
+    L.v_scale = v_scale;
+    L.src = src_blocks;
+    L.dst = dst_blocks;
+    L.num_pairs = num_pairs;
+    L.num_blocks = cache->num_blocks;
+    L.num_kv_heads = cache->num_kv_heads;
+    L.block_size = cache->block_size;
+    L.head_dim = cache->head_dim;
+    L.elem_size = cache->kv_dtype == PKV_F32 ? 4 : cache->kv_dtype == PKV_BF16 ? 2 : 1;
+    const hipError_t e = pkv::launch_copy_blocks(L, st);
+    return e == hipSuccess ? PKV_OK : hip_fail(e, "kv_cache_copy_blocks launch");
 }
 
 }  // extern "C"

@@ -18,6 +18,10 @@ inline hipError_t launch(void (*kern)(Params...), dim3 grid, dim3 block, size_t 
     return hipLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, ptrs, shmem, stream);
 }
 
+// Set this thread's pkv_last_error() text and return `status`.
+int report(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+
 // Compute units and per-kernel occupancy of the current device (cached).
 int device_cu_count();
 
@@ -81,5 +85,26 @@ struct PrefillLaunch {
     int32_t window;
 };
 hipError_t launch_prefill(const PrefillLaunch& L, hipStream_t stream);
+
+struct SlotMappingLaunch {
+    const int32_t* cu_q_lens;
+    const int32_t* seq_lens;
+    const int32_t* block_tables;
+    int32_t num_seqs, max_blocks_per_seq, block_size, num_blocks;
+    int32_t* slot_mapping;
+    int32_t total_rows;
+};
+hipError_t launch_slot_mapping(const SlotMappingLaunch& L, hipStream_t stream);
+
+struct CopyBlocksLaunch {
+    void* k_pool;
+    void* v_pool;
+    void* k_scale;             // INT8 pools only, else null
+    void* v_scale;
+    const int32_t* src;
+    const int32_t* dst;
+    int32_t num_pairs, num_blocks, num_kv_heads, block_size, head_dim, elem_size;
+};
+hipError_t launch_copy_blocks(const CopyBlocksLaunch& L, hipStream_t stream);
 
 }  // namespace pkv
