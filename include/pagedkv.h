@@ -181,7 +181,13 @@ int paged_attention_decode(const pkv_cache_desc* cache,
  *   block_tables  as for decode; with a window, entries wholly before the
  *                 first row's window may be -1 (evicted): they hold no key
  *                 any row can see.
- * Pools must be BF16.  num_seqs == 0 or max_q_len == 0 is a no-op.
+ *   k_scale/v_scale  INT8 pools only (16-byte aligned), else NULL.
+ * Pools are BF16 or INT8 ("MicroGen", Key Features: dynamic per-vector INT8
+ * KV).  INT8 keys enter the scores exactly (code . q times the key's scale);
+ * each V scale is folded into its key's softmax weight, carried in two fp16
+ * parts (~22 significant bits).  Weights reach 256 before a rescale, so V
+ * scales must be <= 255 (|values| <= 32385).
+ * num_seqs == 0 or max_q_len == 0 is a no-op.
  */
 int paged_attention_prefill_chunk(const pkv_cache_desc* cache,
                                   const void* q, int32_t q_dtype,
@@ -189,6 +195,7 @@ int paged_attention_prefill_chunk(const pkv_cache_desc* cache,
                                   const int32_t* cu_q_lens, int32_t num_seqs,
                                   int32_t max_q_len, int32_t num_q_heads,
                                   const void* k_pool, const void* v_pool,
+                                  const void* k_scale, const void* v_scale,
                                   const int32_t* block_tables, int32_t max_blocks_per_seq,
                                   const int32_t* seq_lens,
                                   float softmax_scale, int32_t sliding_window,

@@ -66,8 +66,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.paged_attention_decode.argtypes = [D, P, i32, P, i32, i32, i32, P, P, P, P, P, i32, P,
                                                    f32, i32, i32, P, ctypes.c_size_t, P]
             lib.paged_attention_prefill_chunk.restype = ctypes.c_int
-            lib.paged_attention_prefill_chunk.argtypes = [D, P, i32, P, i32, P, i32, i32, i32, P, P, P, i32,
-                                                          P, f32, i32, P]
+            lib.paged_attention_prefill_chunk.argtypes = [D, P, i32, P, i32, P, i32, i32, i32, P, P, P, P, P,
+                                                          i32, P, f32, i32, P]
             lib.pkv_last_error.restype = ctypes.c_char_p
             lib.pkv_last_error.argtypes = []
             lib.pkv_version.restype = ctypes.c_char_p
@@ -236,10 +236,12 @@ def paged_attention_prefill_chunk(q: torch.Tensor, cu_q_lens: torch.Tensor, seq_
                                   k_pool: torch.Tensor, v_pool: torch.Tensor, block_tables: torch.Tensor,
                                   max_q_len: int, softmax_scale: float, sliding_window: int = 0,
                                   out: torch.Tensor | None = None,
-                                  out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
-    """Chunked-prefill attention for q [total_rows][Hq][D] (bf16)."""
-    dev = _on_gpu(q, cu_q_lens, seq_lens, k_pool, v_pool, block_tables, out)
-    _check_pools(k_pool, v_pool, None, None)
+                                  out_dtype: torch.dtype = torch.float32,
+                                  k_scale: torch.Tensor | None = None,
+                                  v_scale: torch.Tensor | None = None) -> torch.Tensor:
+    """Chunked-prefill attention for q [total_rows][Hq][D] (bf16) over bf16 or INT8 pools."""
+    dev = _on_gpu(q, cu_q_lens, seq_lens, k_pool, v_pool, block_tables, out, k_scale, v_scale)
+    _check_pools(k_pool, v_pool, k_scale, v_scale)
     desc = cache_desc(k_pool)
     _contig(q, "q")
     if q.dim() != 3 or q.shape[2] != desc.head_dim:
@@ -261,7 +263,7 @@ def paged_attention_prefill_chunk(q: torch.Tensor, cu_q_lens: torch.Tensor, seq_
     lib = load_library()
     _check(lib.paged_attention_prefill_chunk(
         ctypes.byref(desc), _ptr(q), _dtype(q, "q"), _ptr(out), _dtype(out, "out"), _ptr(cu_q_lens), b,
-        int(max_q_len), q.shape[1], _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+        int(max_q_len), q.shape[1], _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
         max(block_tables.shape[1], 1), _ptr(seq_lens), float(softmax_scale), int(sliding_window), _stream(dev)))
     return out
 

@@ -303,7 +303,8 @@ int paged_attention_decode(const pkv_cache_desc* cache, const void* q, int32_t q
 int paged_attention_prefill_chunk(const pkv_cache_desc* cache, const void* q, int32_t q_dtype, void* out,
                                   int32_t out_dtype, const int32_t* cu_q_lens, int32_t num_seqs,
                                   int32_t max_q_len, int32_t num_q_heads, const void* k_pool,
-                                  const void* v_pool, const int32_t* block_tables,
+                                  const void* v_pool, const void* k_scale, const void* v_scale,
+                                  const int32_t* block_tables,
                                   int32_t max_blocks_per_seq, const int32_t* seq_lens, float softmax_scale,
                                   int32_t sliding_window, void* stream) {
     g_error.clear();
@@ -320,7 +321,13 @@ int paged_attention_prefill_chunk(const pkv_cache_desc* cache, const void* q, in
     if (!std::isfinite(softmax_scale) || softmax_scale < 0.0f)
         return fail(PKV_EINVAL, "softmax_scale must be finite and >= 0");
     if (q_dtype != PKV_BF16) return fail(q_dtype == PKV_F32 ? PKV_EUNSUPPORTED : PKV_EINVAL, "prefill needs BF16 q");
-    if (cache->kv_dtype != PKV_BF16) return fail(PKV_EUNSUPPORTED, "prefill needs a BF16 pool (got %s)", dtype_name(cache->kv_dtype));
+    const bool i8 = cache->kv_dtype == PKV_I8;
+    if (cache->kv_dtype != PKV_BF16 && !i8)
+        return fail(PKV_EUNSUPPORTED, "prefill needs a BF16 or INT8 pool (got %s)", dtype_name(cache->kv_dtype));
+    if (i8 && (!k_scale || !v_scale)) return fail(PKV_EINVAL, "INT8 pools need k_scale and v_scale");
+    if (!i8 && (k_scale || v_scale)) return fail(PKV_EINVAL, "k_scale/v_scale must be NULL for %s pools", dtype_name(cache->kv_dtype));
+    if (i8 && (!aligned(k_scale, 16) || !aligned(v_scale, 16)))
+        return fail(PKV_EINVAL, "INT8 scale pools must be 16-byte aligned for prefill");
     if (out_dtype != PKV_F32 && out_dtype != PKV_BF16) return fail(PKV_EUNSUPPORTED, "out_dtype must be F32 or BF16");
     if ((int64_t)max_q_len * (num_q_heads / cache->num_kv_heads) > INT32_MAX / 2)
         return fail(PKV_EUNSUPPORTED, "max_q_len too large");
@@ -349,6 +356,9 @@ int paged_attention_prefill_chunk(const pkv_cache_desc* cache, const void* q, in
     L.num_blocks = cache->num_blocks;
     L.k_pool = k_pool;
     L.v_pool = v_pool;
+    L.int8 = i8;
+    L.k_scale = static_cast<const uint16_t*>(k_scale);
+    L.v_scale = static_cast<const uint16_t*>(v_scale);
     L.block_tables = block_tables;
     L.max_blocks_per_seq = max_blocks_per_seq;
     L.seq_lens = seq_lens;

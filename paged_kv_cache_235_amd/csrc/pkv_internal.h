@@ -76,8 +76,11 @@ struct PrefillLaunch {
     bool out_bf16;
     const int32_t* cu_q_lens;
     int32_t num_seqs, max_q_len, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks;
-    const void* k_pool;        // bf16
+    const void* k_pool;        // bf16, or int8 codes
     const void* v_pool;
+    bool int8;
+    const uint16_t* k_scale;   // INT8 pools: fp16 scales, else null
+    const uint16_t* v_scale;
     const int32_t* block_tables;
     int32_t max_blocks_per_seq;
     const int32_t* seq_lens;

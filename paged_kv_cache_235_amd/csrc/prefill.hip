@@ -37,6 +37,20 @@
 //    rescale (the output is rescaled only when a row maximum grows by > 2^8).
 //  * Workgroups of one (sequence, KV head) are placed on the same XCD so the
 //    K/V tiles they all read stay in that XCD's L2.
+//
+// INT8 pools ("MicroGen", Key Features: dynamic per-vector INT8 KV): K codes
+// are staged as bf16 (integers up to 127 are exact), so Q.K^T of the codes is
+// the same MFMA, and each score column is then multiplied by its key's scale
+// (times softmax scale * log2 e, staged per tile in LDS): the dequantised
+// logit without rounding K.  V codes are staged as exact fp16 integers and
+// each key's V scale goes into its weight: w = p * scale (fp32) is carried as
+// an fp16 value plus its fp16 remainder, and P.V takes one MFMA for each, so
+// the weights keep ~22 significant bits (one fp16 rounding of w moves the
+// output by up to ~2^-12 |v|, which the 1% x8 outliers make visible); the row
+// sum adds the fp32 p.  Weights and P.V go one 16-key k-step at a time so the
+// remainders add little to the registers live at once.
+#include <type_traits>
+
 #include "pkv_internal.h"
 #include "pkv_device.h"
 
@@ -52,8 +66,10 @@ constexpr int kXcds = 8;
 struct PrefillArgs {
     const uint16_t* q;
     void* out;
-    const uint16_t* k_pool;
-    const uint16_t* v_pool;
+    const void* k_pool;         // bf16, or int8 codes
+    const void* v_pool;
+    const uint16_t* k_scale;    // INT8 pools: fp16 scales [blocks][heads][16]
+    const uint16_t* v_scale;
     const int32_t* block_tables;
     const int32_t* seq_lens;
     const int32_t* cu_q_lens;
@@ -79,8 +95,9 @@ __device__ __forceinline__ int vt_col(int d, int g) { return ((g ^ ((d >> 4) & 7
 
 // W waves (32 query rows each) share double-buffered K/V tiles; each wave
 // issues the next tile's S^T = K Q^T MFMAs with this tile's softmax.
-template <int D, int W, bool ZS>
+template <int D, int W, bool ZS, bool I8>
 __global__ __launch_bounds__(64 * W) void prefill_pipe_kernel(PrefillArgs a) {
+    using KT = typename std::conditional<I8, int8_t, uint16_t>::type;   // pool element
     constexpr int NTH = 64 * W;                 // threads
     constexpr int ROWS = 32 * W;                // query rows per workgroup
     constexpr int KS = D + 8;                   // halfwords per K row in LDS
@@ -93,6 +110,8 @@ __global__ __launch_bounds__(64 * W) void prefill_pipe_kernel(PrefillArgs a) {
     static_assert(KCH >= 1 && NTH % KPB == 0 && VPIECES <= NTH, "staging shape");
     __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kKeys * KS];
     __shared__ __attribute__((aligned(16))) uint16_t s_vt[2][D * kVtStride];   // V^T as fp16
+    __shared__ __attribute__((aligned(16))) float s_ksc[I8 ? 2 : 1][I8 ? kKeys : 4];  // K scale * scale_log2
+    __shared__ __attribute__((aligned(16))) float s_vsc[I8 ? 2 : 1][I8 ? kKeys : 4];  // V scale
 
     // ---- work item: XCD-major so that one (sequence, head) stays on one XCD
     const int per_xcd = (a.total + kXcds - 1) / kXcds;
@@ -161,8 +180,10 @@ __global__ __launch_bounds__(64 * W) void prefill_pipe_kernel(PrefillArgs a) {
     const int v_kg = (tid / (D / 2)) & 7;
     const int k_off = ((tid / (D / 8)) % kBlk) * D + (tid % (D / 8)) * 8;
     const int v_off = ((8 * v_kg) % kBlk) * D + 2 * v_dp;
-    u32x4_t kreg[KCH];
-    uint32_t vreg[8];
+    u32x4_t kreg[I8 ? 1 : KCH];          // bf16: 8 elements per chunk
+    u32x2_t kreg8[I8 ? KCH : 1];         // INT8: 8 codes per chunk
+    uint32_t vreg[I8 ? 4 : 8];           // bf16: 2 elements of key i; INT8: 2 codes of keys 2i, 2i + 1
+    uint32_t ksreg = 0, vsreg = 0;      // INT8: fp16 K and V scales of key tid (wave 0)
     int id0 = 0, id1 = 0, id2 = 0, id3 = 0;     // physical blocks of the staged tile (0 when invalid)
 
     auto kt_of = [&](int t) { return kt_first + kKeys * t; };
@@ -181,17 +202,40 @@ __global__ __launch_bounds__(64 * W) void prefill_pipe_kernel(PrefillArgs a) {
         return m;
     };
     auto sel = [&](int b) { return b == 0 ? id0 : (b == 1 ? id1 : (b == 2 ? id2 : id3)); };
-    auto blk_base = [&](const uint16_t* pool, int id) { return pool + (int64_t)id * blk_stride + g * head_stride; };
+    auto blk_base = [&](const void* pool, int id) {
+        return static_cast<const KT*>(pool) + (int64_t)id * blk_stride + g * head_stride;
+    };
+    // INT8 scale of (block id, this head, offset)
+    auto scale_at = [&](const uint16_t* sc, int id, int off) {
+        return sc + ((int64_t)id * a.num_kv_heads + g) * kBlk + off;
+    };
     auto load_tile = [&]() {
 #pragma unroll
         for (int i = 0; i < KCH; ++i) {
             const int id = sel((NTH * i) / KPB + tid / KPB);
-            kreg[i] = *reinterpret_cast<const u32x4_t*>(blk_base(a.k_pool, id) + k_off);
+            if constexpr (I8) {
+                kreg8[i] = *reinterpret_cast<const u32x2_t*>(blk_base(a.k_pool, id) + k_off);
+            } else {
+                kreg[i] = *reinterpret_cast<const u32x4_t*>(blk_base(a.k_pool, id) + k_off);
+            }
         }
         if (v_task) {
-            const uint16_t* vp = blk_base(a.v_pool, sel(v_kg / 2)) + v_off;
+            const KT* vp = blk_base(a.v_pool, sel(v_kg / 2)) + v_off;
+            if constexpr (I8) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) vreg[i] = *reinterpret_cast<const uint32_t*>(vp + i * D);
+                for (int i = 0; i < 4; ++i)
+                    vreg[i] = (uint32_t)*reinterpret_cast<const uint16_t*>(vp + 2 * i * D) |
+                              ((uint32_t)*reinterpret_cast<const uint16_t*>(vp + (2 * i + 1) * D) << 16);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) vreg[i] = *reinterpret_cast<const uint32_t*>(vp + i * D);
+            }
+        }
+        if constexpr (I8) {
+            if (tid < kKeys) {
+                ksreg = *scale_at(a.k_scale, sel(tid / kBlk), tid % kBlk);
+                vsreg = *scale_at(a.v_scale, sel(tid / kBlk), tid % kBlk);
+            }
         }
     };
     auto store_tile = [&](int buf, int kt, int m) {
@@ -199,9 +243,44 @@ __global__ __launch_bounds__(64 * W) void prefill_pipe_kernel(PrefillArgs a) {
         for (int i = 0; i < KCH; ++i) {
             const int c = tid + NTH * i;
             const int key = c / (D / 8), dc = c % (D / 8);
-            *reinterpret_cast<u32x4_t*>(&s_k[buf][swap23(key) * KS + dc * 8]) = kreg[i];
+            u32x4_t kv;
+            if constexpr (I8) {
+                // 8 codes -> 8 bf16 integers (exact): the top half of each code's fp32
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const uint32_t word = kreg8[i][w >> 1] >> (16 * (w & 1));
+                    const float lo = (float)(int8_t)(word & 0xffu);
+                    const float hi = (float)(int8_t)((word >> 8) & 0xffu);
+                    kv[w] = (__builtin_bit_cast(uint32_t, lo) >> 16) | (__builtin_bit_cast(uint32_t, hi) & 0xffff0000u);
+                }
+            } else {
+                kv = kreg[i];
+            }
+            *reinterpret_cast<u32x4_t*>(&s_k[buf][swap23(key) * KS + dc * 8]) = kv;
         }
-        if (v_task) {
+        if constexpr (I8) {
+            if (tid < kKeys) {
+                // keys past the sequence or in a missing block may hold NaN scales: 0
+                const bool live = ((m >> (tid / kBlk)) & 1) && kt + tid < L;
+                const float ks = (float)__builtin_bit_cast(_Float16, (uint16_t)ksreg);
+                const float vs = (float)__builtin_bit_cast(_Float16, (uint16_t)vsreg);
+                s_ksc[buf][tid] = live ? ks * a.scale_log2 : 0.0f;
+                s_vsc[buf][tid] = live ? vs : 0.0f;
+            }
+            if (v_task) {
+                // 8 keys x 2 dims -> 2 rows of 8 keys, the codes as exact fp16
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    u32x4_t r;
+#pragma unroll
+                    for (int mm = 0; mm < 4; ++mm)
+                        r[mm] = pack_f16x2((float)(int8_t)((vreg[mm] >> (8 * e)) & 0xffu),
+                                           (float)(int8_t)((vreg[mm] >> (16 + 8 * e)) & 0xffu));
+                    const int d = 2 * v_dp + e;
+                    *reinterpret_cast<u32x4_t*>(&s_vt[buf][d * kVtStride + vt_col(d, v_kg)]) = r;
+                }
+            }
+        } else if (v_task) {
             uint32_t w[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) w[i] = vreg[i];
@@ -254,7 +333,27 @@ __global__ __launch_bounds__(64 * W) void prefill_pipe_kernel(PrefillArgs a) {
     // the same basic block as the exp2 work so the two overlap.  On the last
     // tile that buffer holds stale data: the MFMAs still read in-bounds LDS and
     // their result is never used.
+    // the factor that turns an accumulated score into log2 units (INT8: the
+    // per-key factor is already applied)
+    const float sl2 = I8 ? 1.0f : a.scale_log2;
     auto finish_tile = [&](f32x16_t* S, f32x16_t* S_nxt, int buf, int kt, int tmask) {
+        if constexpr (I8) {
+            // score of key j times scale_j * softmax scale * log2 e (before masking: a
+            // dead key's NaN scale is then selected away)
+            const float* kp = &s_ksc[buf][8 * h];
+#pragma unroll
+            for (int T = 0; T < 2; ++T)
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const f32x4_t f0 = *reinterpret_cast<const f32x4_t*>(kp + 32 * T + 16 * u);
+                    const f32x4_t f1 = *reinterpret_cast<const f32x4_t*>(kp + 32 * T + 16 * u + 4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        S[T][8 * u + e] *= f0[e];
+                        S[T][8 * u + 4 + e] *= f1[e];
+                    }
+                }
+        }
         // masks (edge tiles only): key of accumulator v = kt + 32T + 16(v/8) + 8h + v%8
         const bool full = tmask == 15 && kt + kKeys - 1 <= p_min && (a.window <= 0 || kt >= p_max - a.window + 1);
         if (!full) {
@@ -275,7 +374,7 @@ __global__ __launch_bounds__(64 * W) void prefill_pipe_kernel(PrefillArgs a) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) mt_ = fmaxf(mt_, S[T][v]);
         mt_ = fmaxf(mt_, __shfl_xor(mt_, 32, kWave));
-        const float m_tile = mt_ == -INFINITY ? -INFINITY : mt_ * a.scale_log2;
+        const float m_tile = mt_ == -INFINITY ? -INFINITY : mt_ * sl2;
         const bool grow = m_tile > m_used + kRescale || (m_used == -INFINITY && m_tile != -INFINITY);
         if (__builtin_amdgcn_ballot_w64(grow)) {
             const float m_new = grow ? m_tile : m_used;
@@ -290,52 +389,92 @@ __global__ __launch_bounds__(64 * W) void prefill_pipe_kernel(PrefillArgs a) {
         }
         const float msub = (m_used == -INFINITY) ? 0.0f : m_used;
         compute_s(S_nxt, buf ^ 1);
-        uint32_t pw[2][8];                       // P^T as fp16 pairs: [T][4u + word]
-        if constexpr (!ZS) {
-            // a masked score (-inf) scales to -inf and exp2 gives 0 by itself
-#pragma unroll
-            for (int T = 0; T < 2; ++T)
-#pragma unroll
-                for (int v = 0; v < 16; v += 2)
-                    pw[T][v / 2] = pack_f16x2(fast_exp2(fmaf(S[T][v], a.scale_log2, -msub)),
-                                              fast_exp2(fmaf(S[T][v + 1], a.scale_log2, -msub)));
-        } else {
-            // scale 0: -inf * 0 would be NaN, so masked scores are selected away
-#pragma unroll
-            for (int T = 0; T < 2; ++T)
-#pragma unroll
-                for (int v = 0; v < 16; v += 2) {
-                    const float x0 = S[T][v], x1 = S[T][v + 1];
-                    const float p0 = (x0 == -INFINITY) ? 0.0f : fast_exp2(fmaf(x0, a.scale_log2, -msub));
-                    const float p1 = (x1 == -INFINITY) ? 0.0f : fast_exp2(fmaf(x1, a.scale_log2, -msub));
-                    pw[T][v / 2] = pack_f16x2(p0, p1);
-                }
-        }
-        // row sum of the fp16 weights -- the values P.V multiplies -- two per dot2
-        {
-            const f16x2_t one = {(_Float16)1.0f, (_Float16)1.0f};
-            float ls0 = 0.0f, ls1 = 0.0f;
-#pragma unroll
-            for (int w = 0; w < 8; ++w) {
-                ls0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pw[0][w]), one, ls0, false);
-                ls1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pw[1][w]), one, ls1, false);
-            }
-            l_run += ls0 + ls1;
-        }
-        // O^T += V^T P^T: k-step ks covers keys 16ks..16ks+15 (tile T = ks/2, u = ks%2);
         // V^T row d = 32 nt + (lane & 31), key group 2 ks + h, at one base + constants
         const uint16_t* vt_base = &s_vt[buf][(lane & 31) * kVtStride + 8 * (h ^ ((lane >> 4) & 1))];
+        if constexpr (I8) {
+            // w = p * V scale as fp16 + fp16 remainder; O^T += V^T W^T for each part.
+            // One k-step (16 keys) at a time: its weights, then its MFMAs.
+            const float* vsp = &s_vsc[buf][8 * h];
+            float ls = 0.0f;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const int T = ks >> 1, u = ks & 1;
-            u32x4_t pb;
-            pb[0] = pw[T][4 * u + 0]; pb[1] = pw[T][4 * u + 1];
-            pb[2] = pw[T][4 * u + 2]; pb[3] = pw[T][4 * u + 3];
+            for (int ks = 0; ks < 4; ++ks) {
+                const int T = ks >> 1, u = ks & 1;
+                const f32x4_t f0 = *reinterpret_cast<const f32x4_t*>(vsp + 32 * T + 16 * u);
+                const f32x4_t f1 = *reinterpret_cast<const f32x4_t*>(vsp + 32 * T + 16 * u + 4);
+                u32x4_t pb, pr;
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const u32x4_t vv = *reinterpret_cast<const u32x4_t*>(
-                    vt_base + 32 * nt * kVtStride + 16 * ((ks ^ nt) & 7));
-                o[nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(vv), as_f16x8(pb), o[nt], 0, 0, 0);
+                for (int e = 0; e < 8; e += 2) {
+                    const float x0 = S[T][8 * u + e], x1 = S[T][8 * u + e + 1];
+                    float p0, p1;
+                    if constexpr (ZS) {
+                        p0 = (x0 == -INFINITY) ? 0.0f : fast_exp2(x0 - msub);
+                        p1 = (x1 == -INFINITY) ? 0.0f : fast_exp2(x1 - msub);
+                    } else {
+                        p0 = fast_exp2(x0 - msub);
+                        p1 = fast_exp2(x1 - msub);
+                    }
+                    ls += p0 + p1;
+                    const float w0 = p0 * (e < 4 ? f0[e] : f1[e - 4]);
+                    const float w1 = p1 * (e < 4 ? f0[e + 1] : f1[e - 3]);
+                    const float h0 = (float)(_Float16)w0, h1 = (float)(_Float16)w1;
+                    pb[e / 2] = pack_f16x2(h0, h1);
+                    pr[e / 2] = pack_f16x2(w0 - h0, w1 - h1);
+                }
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    const u32x4_t vv = *reinterpret_cast<const u32x4_t*>(
+                        vt_base + 32 * nt * kVtStride + 16 * ((ks ^ nt) & 7));
+                    o[nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(vv), as_f16x8(pb), o[nt], 0, 0, 0);
+                    o[nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(vv), as_f16x8(pr), o[nt], 0, 0, 0);
+                }
+            }
+            l_run += ls;
+        } else {
+            uint32_t pw[2][8];                       // P^T as fp16 pairs: [T][4u + word]
+            if constexpr (!ZS) {
+                // a masked score (-inf) scales to -inf and exp2 gives 0 by itself
+#pragma unroll
+                for (int T = 0; T < 2; ++T)
+#pragma unroll
+                    for (int v = 0; v < 16; v += 2)
+                        pw[T][v / 2] = pack_f16x2(fast_exp2(fmaf(S[T][v], sl2, -msub)),
+                                                  fast_exp2(fmaf(S[T][v + 1], sl2, -msub)));
+            } else {
+                // scale 0: -inf * 0 would be NaN, so masked scores are selected away
+#pragma unroll
+                for (int T = 0; T < 2; ++T)
+#pragma unroll
+                    for (int v = 0; v < 16; v += 2) {
+                        const float x0 = S[T][v], x1 = S[T][v + 1];
+                        const float p0 = (x0 == -INFINITY) ? 0.0f : fast_exp2(fmaf(x0, sl2, -msub));
+                        const float p1 = (x1 == -INFINITY) ? 0.0f : fast_exp2(fmaf(x1, sl2, -msub));
+                        pw[T][v / 2] = pack_f16x2(p0, p1);
+                    }
+            }
+            // row sum of the fp16 weights -- the values P.V multiplies -- two per dot2
+            {
+                const f16x2_t one = {(_Float16)1.0f, (_Float16)1.0f};
+                float ls0 = 0.0f, ls1 = 0.0f;
+#pragma unroll
+                for (int w = 0; w < 8; ++w) {
+                    ls0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pw[0][w]), one, ls0, false);
+                    ls1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pw[1][w]), one, ls1, false);
+                }
+                l_run += ls0 + ls1;
+            }
+            // O^T += V^T P^T: k-step ks covers keys 16ks..16ks+15 (tile T = ks/2, u = ks%2)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int T = ks >> 1, u = ks & 1;
+                u32x4_t pb;
+                pb[0] = pw[T][4 * u + 0]; pb[1] = pw[T][4 * u + 1];
+                pb[2] = pw[T][4 * u + 2]; pb[3] = pw[T][4 * u + 3];
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    const int off = 32 * nt * kVtStride + 16 * ((ks ^ nt) & 7);
+                    const u32x4_t vv = *reinterpret_cast<const u32x4_t*>(vt_base + off);
+                    o[nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(vv), as_f16x8(pb), o[nt], 0, 0, 0);
+                }
             }
         }
     };
@@ -415,8 +554,10 @@ hipError_t launch_prefill(const PrefillLaunch& L, hipStream_t stream) {
     PrefillArgs a;
     a.q = static_cast<const uint16_t*>(L.q);
     a.out = L.out;
-    a.k_pool = static_cast<const uint16_t*>(L.k_pool);
-    a.v_pool = static_cast<const uint16_t*>(L.v_pool);
+    a.k_pool = L.k_pool;
+    a.v_pool = L.v_pool;
+    a.k_scale = L.k_scale;
+    a.v_scale = L.v_scale;
     a.block_tables = L.block_tables;
     a.seq_lens = L.seq_lens;
     a.cu_q_lens = L.cu_q_lens;
@@ -439,11 +580,18 @@ hipError_t launch_prefill(const PrefillLaunch& L, hipStream_t stream) {
     const int64_t grid = ((total + kXcds - 1) / kXcds) * kXcds;
     const dim3 g3((unsigned)grid), b3(64 * kPipeWaves);
     const bool zs = !(a.scale_log2 > 0.0f);
+    if (L.int8) {
+        if (L.head_dim == 64)
+            return zs ? launch(prefill_pipe_kernel<64, kPipeWaves, true, true>, g3, b3, 0, stream, a)
+                      : launch(prefill_pipe_kernel<64, kPipeWaves, false, true>, g3, b3, 0, stream, a);
+        return zs ? launch(prefill_pipe_kernel<128, kPipeWaves, true, true>, g3, b3, 0, stream, a)
+                  : launch(prefill_pipe_kernel<128, kPipeWaves, false, true>, g3, b3, 0, stream, a);
+    }
     if (L.head_dim == 64)
-        return zs ? launch(prefill_pipe_kernel<64, kPipeWaves, true>, g3, b3, 0, stream, a)
-                  : launch(prefill_pipe_kernel<64, kPipeWaves, false>, g3, b3, 0, stream, a);
-    return zs ? launch(prefill_pipe_kernel<128, kPipeWaves, true>, g3, b3, 0, stream, a)
-              : launch(prefill_pipe_kernel<128, kPipeWaves, false>, g3, b3, 0, stream, a);
+        return zs ? launch(prefill_pipe_kernel<64, kPipeWaves, true, false>, g3, b3, 0, stream, a)
+                  : launch(prefill_pipe_kernel<64, kPipeWaves, false, false>, g3, b3, 0, stream, a);
+    return zs ? launch(prefill_pipe_kernel<128, kPipeWaves, true, false>, g3, b3, 0, stream, a)
+              : launch(prefill_pipe_kernel<128, kPipeWaves, false, false>, g3, b3, 0, stream, a);
 }
 
 }  // namespace pkv

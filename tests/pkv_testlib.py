@@ -107,7 +107,8 @@ def run_prefill(case, pools, dev, **kw):
     bt, lens, cu = tables(case, dev)
     q = case.q(dev)
     return pkv.paged_attention_prefill_chunk(q, cu, lens, pools["k"], pools["v"], bt, case.max_q_len,
-                                             case.softmax_scale, sliding_window=case.window, **kw)
+                                             case.softmax_scale, sliding_window=case.window,
+                                             k_scale=pools["ks"], v_scale=pools["vs"], **kw)
 
 
 def assert_close(got: torch.Tensor, ref: np.ndarray, dtype: str, what: str = ""):

@@ -111,14 +111,19 @@ def test_prefill_validation(lib):
     p = lib.paged_attention_prefill_chunk
     d = _desc()
     args = lambda **k: (ctypes.byref(k.get("desc", d)), FAKE, k.get("qd", BF16), FAKE, F32, FAKE,
-                        k.get("b", 2), k.get("mq", 16), k.get("hq", 8), FAKE, FAKE, FAKE, 4, FAKE, 0.1,
-                        k.get("w", 0), None)
+                        k.get("b", 2), k.get("mq", 16), k.get("hq", 8), FAKE, FAKE, k.get("ks"), k.get("vs"),
+                        FAKE, 4, FAKE, 0.1, k.get("w", 0), None)
     assert p(*args(b=0)) == PKV_OK
     assert p(*args(mq=0)) == PKV_OK
     assert p(*args(qd=F32)) == PKV_EUNSUPPORTED
     assert p(*args(desc=_desc(dt=F32))) == PKV_EUNSUPPORTED
     assert p(*args(hq=5)) == PKV_EINVAL
     assert p(*args(w=-3)) == PKV_EINVAL
+    # INT8 pools need both scale pools; other pools take none
+    assert p(*args(desc=_desc(dt=I8))) == PKV_EINVAL
+    assert p(*args(desc=_desc(dt=I8), ks=FAKE)) == PKV_EINVAL
+    assert p(*args(desc=_desc(dt=I8), ks=FAKE, vs=FAKE, b=0)) == PKV_OK
+    assert p(*args(ks=FAKE, vs=FAKE)) == PKV_EINVAL
 
 
 def test_version(lib):

@@ -105,3 +105,65 @@ def test_prefill_zero_scale_and_empty_chunks():
                                window=10, kind="prefill")
     out, _ = _gpu(case)
     assert_close(out, expected_outputs(case), "bf16")
+
+
+# ---------------------------------------------------------------- INT8 pools
+def _i8(seq_lens, new_lens, hq=8, hkv=2, d=128, window=0, seed=91, **kw):
+    return workloads.make_case("prefill-i8", seed, seq_lens, new_lens, hq, hkv, d, kv_dtype="i8",
+                               outliers=0.01, window=window, kind="prefill", **kw)
+
+
+@pytest.mark.parametrize("lens,new", SHAPES, ids=["from0", "small", "mid", "long"])
+@pytest.mark.parametrize("window", [0, 17, 512])
+def test_int8_prefill_matches_dequantised_oracle(lens, new, window):
+    """K/V written through the quantising cache write (1% x8 outliers); the
+    oracle attends over the same dequantised cache ("MicroGen", Key Features:
+    dynamic INT8 KV)."""
+    case = _i8(lens, new, window=window)
+    out, _ = _gpu(case)
+    assert_close(out, expected_outputs(case), "bf16", f"int8 W={window}")
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(8, 2, 64), (12, 2, 128), (5, 5, 64), (32, 8, 128)])
+def test_int8_prefill_geometries_and_cosine(hq, hkv, d):
+    case = _i8([300, 77, 1100], [130, 77, 40], hq=hq, hkv=hkv, d=d, window=200)
+    out, _ = _gpu(case)
+    assert_close(out, expected_outputs(case), "bf16", "int8")
+    ref_f = expected_outputs(case, kv_dtype="bf16")        # the same K/V unquantised
+    a = out.double().cpu().numpy().reshape(-1, d)
+    b = ref_f.reshape(-1, d)
+    cos = (a * b).sum(1) / np.linalg.norm(a, axis=1) / np.linalg.norm(b, axis=1)
+    assert cos.min() > 0.98, cos.min()
+
+
+def test_int8_prefill_zero_scale_empty_chunks_and_bf16_output():
+    case = _i8([50, 20, 70], [0, 20, 5], window=10, softmax_scale=0.0)
+    out, _ = _gpu(case)
+    assert_close(out, expected_outputs(case), "bf16", "int8 zero scale")
+    case = _i8([400, 90], [200, 90], window=128)
+    out, _ = _gpu(case, out_dtype=torch.bfloat16)
+    ref = expected_outputs(case)
+    got = out.float().cpu().double().numpy()
+    assert (np.abs(got - ref) <= bf16_ulp(ref) + 2e-3).all()
+
+
+def test_int8_prefill_window_4096_full_size_sampled_rows():
+    """The window-4096 launch (16 x 256 rows on 1024..16384-token contexts,
+    32 q / 8 kv heads) over an INT8 pool; sampled rows against the oracle's
+    decode over the matching prefix of the dequantised cache."""
+    import dataclasses
+    case = dataclasses.replace(workloads.prefill_window(), kv_dtype="i8", outliers=0.01)
+    out, _ = _gpu(case)
+    assert torch.isfinite(out).all()
+    picks = sorted({int(np.argmin(case.seq_lens)), int(np.argmax(case.seq_lens)), 6})
+    sub = case.subset(picks)
+    cache = build_cache(sub, device=device())
+    q = to_numpy(sub.q(device()))
+    cu_full = case.cu_q_lens
+    for si, s in enumerate(picks):
+        L, C = int(case.seq_lens[s]), int(case.new_lens[s])
+        for i in (0, 31, 64, 127, 128, 255):
+            row = int(sub.cu_q_lens[si]) + i
+            ref = oracle.decode(cache, q[row:row + 1], "bf16", np.array([L - C + i + 1], np.int32),
+                                sub.block_tables[si:si + 1], sub.softmax_scale, sub.window)
+            assert_close(out[cu_full[s] + i:cu_full[s] + i + 1], ref, "bf16", f"int8 seq {s} row {i}")
