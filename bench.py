@@ -11,7 +11,11 @@ timed in the same run and reported under "prefill".
 The line printed last is one JSON object: the step's algorithmic KV bytes per
 second ("value"), the decode partition kernel against the HBM roofline
 (timed with HIP events on the launch stream), and the fp64 oracle timed on the
-host ("cpu_baseline").
+host ("cpu_baseline").  Also reported: the same prefill call over an INT8
+pool ("prefill_int8"), the smaller decode workloads (tiny fp32, Qwen2.5-1.5B
+shaped bf16, INT8 KV; back to back and after a cache flush: "decode_shapes"),
+and the slot-mapping and block-copy kernels ("block_ops").  Every timed
+configuration is checked against the oracle on sampled outputs.
 """
 from __future__ import annotations
 
@@ -254,9 +258,12 @@ def prefill_flops(case):
     return 4 * case.head_dim * case.num_q_heads * total
 
 
-def bench_prefill(args, torch, pkv, workloads, tl):
+def bench_prefill(args, torch, pkv, workloads, tl, kv_dtype="bf16"):
     dev = torch.device("cuda", 0)
     case = workloads.prefill_window()
+    if kv_dtype == "i8":
+        import dataclasses
+        case = dataclasses.replace(case, kv_dtype="i8", outliers=0.01)
     pools = tl.alloc_pools(case, dev)
     tl.write_tokens(case, pools, dev, "all")      # the chunk's own tokens are rewritten before each call
     bt, lens, cu = tl.tables(case, dev)
@@ -268,9 +275,10 @@ def bench_prefill(args, torch, pkv, workloads, tl):
 
     def call():
         pkv.paged_attention_prefill_chunk(q, cu, lens, pools["k"], pools["v"], bt, case.max_q_len,
-                                          case.softmax_scale, sliding_window=case.window, out=out)
+                                          case.softmax_scale, sliding_window=case.window, out=out,
+                                          k_scale=pools["ks"], v_scale=pools["vs"])
 
-    pkv.kv_cache_write(new_k, new_v, new_slots, pools["k"], pools["v"])
+    pkv.kv_cache_write(new_k, new_v, new_slots, pools["k"], pools["v"], pools["ks"], pools["vs"])
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
@@ -294,16 +302,148 @@ def bench_prefill(args, torch, pkv, workloads, tl):
     fl = prefill_flops(case)
     sec = float(np.mean(t)) / 1e3
     tf = fl / sec / 1e12
+    kern = "prefill_pipe_kernel<D=128, 8 waves>" if kv_dtype == "bf16" else "prefill_pipe_kernel<D=128, 8 waves, INT8>"
     return {"workload": "chunked prefill: 16 sequences x 256 new tokens on 1024..16384-token paged "
-                        "contexts, 32 q / 8 kv heads, head_dim 128, bf16, causal + window 4096",
+                        f"contexts, 32 q / 8 kv heads, head_dim 128, {kv_dtype} pool, causal + window 4096",
             "us_per_call": round(sec * 1e6, 2), "us_p10": round(float(np.percentile(t, 10)) * 1e3, 2),
             "us_p90": round(float(np.percentile(t, 90)) * 1e3, 2),
-            "roofline": {"kernel": "prefill_pipe_kernel<D=128, 8 waves>", "bound": "mfma", "achieved": round(tf, 1),
+            "roofline": {"kernel": kern, "bound": "mfma", "achieved": round(tf, 1),
                          "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
-                         "traffic": read_traffic("prefill_window", "prefill.hip"),
+                         "traffic": read_traffic("prefill_window" if kv_dtype == "bf16" else "prefill_window_int8",
+                                                 "prefill.hip"),
                          "algorithmic_flops_per_launch": fl},
             "max_abs_err": float(err)}
+
+
+# ------------------------------------------------------------------ other decode shapes
+def back_to_back_us(torch, fn, n):
+    """GPU time per call of n calls queued back to back: the GPU is held by a
+    spin kernel while the host queues them, so host launch cost is not timed."""
+    torch.cuda._sleep(20_000_000)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(n):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / n
+
+
+def bench_decode_shapes(args, torch, pkv, workloads, tl):
+    """The smaller decode workloads at several partition sizes: calls back to
+    back (their K/V, a few MB, stay in the 256 MB last-level cache: 'warm') and
+    one at a time after a 1 GiB write that evicts them ('cold', from HBM).  Each
+    configuration is checked against the oracle."""
+    from oracle.cases import expected_outputs
+    dev = torch.device("cuda", 0)
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    res = {}
+    for name, make in (("tiny fp32 decode (4 seqs, 4 q / 2 kv, D 64)", workloads.tiny_fp32_decode),
+                       ("Qwen2.5-1.5B-shaped bf16 decode (8 seqs, 12 q / 2 kv, D 128)", workloads.qwen_decode),
+                       ("INT8-KV decode (64 seqs, Qwen2.5-1.5B shapes, 1% x8 outliers)", workloads.int8_decode)):
+        case = make()
+        pools = tl.alloc_pools(case, dev)
+        tl.write_tokens(case, pools, dev, "all")
+        bt, lens, _ = tl.tables(case, dev)
+        q = case.q(dev)
+        out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+        from oracle.cases import build_cache
+        ref = expected_outputs(case, cache=build_cache(case, device=dev))
+        by = decode_bytes(case)
+        nbytes = sum(by.values())
+        entry = {"workload": name, "context_tokens": int(case.seq_lens.sum()), "algorithmic_bytes": nbytes,
+                 "by_partition_size": {}}
+        for part in (64, 128, 256, 512):
+            ws = pkv.decode_workspace_size(case.num_seqs, case.num_q_heads, case.head_dim,
+                                           case.max_blocks_per_seq, case.block_size, part)
+            workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+
+            def call():
+                pkv.paged_attention_decode(q, pools["k"], pools["v"], bt, lens, case.softmax_scale,
+                                           sliding_window=case.window, partition_size=part,
+                                           k_scale=pools["ks"], v_scale=pools["vs"], out=out, workspace=workspace)
+
+            for _ in range(args.warmup):
+                call()
+            torch.cuda.synchronize()
+            n = max(args.steps, 20)
+            REGIONS.resume()
+            warm = back_to_back_us(torch, call, n)
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+            for a, b in ev:                       # cold: the cache evicted first
+                flush.fill_(1.0)
+                a.record()
+                call()
+                b.record()
+            torch.cuda.synchronize()
+            REGIONS.pause()
+            cold = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
+            err = tl.assert_close(out, ref, "f32" if case.kv_dtype == "f32" else "bf16", f"{name} P={part}")
+            entry["by_partition_size"][part] = {
+                "warm_us": round(warm, 2), "warm_GB/s": round(nbytes / (warm / 1e6) / 1e9, 1),
+                "cold_us_median": round(cold, 2), "cold_GB/s": round(nbytes / (cold / 1e6) / 1e9, 1),
+                "max_abs_err": float(err)}
+        best = min(entry["by_partition_size"], key=lambda k: entry["by_partition_size"][k]["cold_us_median"])
+        entry["best_partition_size_cold"] = best
+        entry["best_cold_frac_of_hbm_peak"] = round(
+            entry["by_partition_size"][best]["cold_GB/s"] / HBM_PEAK_GBS, 4)
+        res[case.name] = entry
+        del pools
+    del flush
+    torch.cuda.empty_cache()
+    return res
+
+
+# ------------------------------------------------------------------ block bookkeeping kernels
+def bench_block_ops(args, torch, pkv, workloads):
+    """Device slot mapping for the two large steps, and a burst of block copies
+    (copy on write of 256 shared Llama-shaped blocks: 8 kv heads x 16 x 128 bf16)."""
+    dev = torch.device("cuda", 0)
+    res = {}
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
+    for tag, case in (("llama3-8b decode step (256 rows)", workloads.llama_decode()),
+                      ("window-4096 prefill step (4096 rows)", workloads.prefill_window())):
+        k_pool = torch.empty((case.num_blocks, 1, 16, 64), dtype=torch.bfloat16, device=dev)   # shape only
+        cu, lens, bt = t(case.cu_q_lens), t(case.seq_lens), t(case.block_tables)
+        out = torch.empty(int(case.cu_q_lens[-1]), dtype=torch.int32, device=dev)
+        for _ in range(args.warmup):
+            pkv.build_slot_mapping(cu, lens, bt, k_pool, out=out)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        REGIONS.resume()
+        for a, b in ev:
+            a.record()
+            pkv.build_slot_mapping(cu, lens, bt, k_pool, out=out)
+            b.record()
+        torch.cuda.synchronize()
+        warm = back_to_back_us(torch, lambda: pkv.build_slot_mapping(cu, lens, bt, k_pool, out=out), args.steps)
+        REGIONS.pause()
+        assert np.array_equal(out.cpu().numpy(), case.new_slots()), tag
+        us = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
+        res["slot_mapping: " + tag] = {"us_median_one_call": round(us, 2), "us_back_to_back": round(warm, 2)}
+    nb, pairs = 4096, 256
+    shape = (nb, 8, 16, 128)
+    k = torch.zeros(shape, dtype=torch.bfloat16, device=dev)
+    v = torch.zeros(shape, dtype=torch.bfloat16, device=dev)
+    perm = np.random.default_rng(0).permutation(nb).astype(np.int32)
+    src, dst = t(perm[:pairs]), t(perm[pairs:2 * pairs])
+    for _ in range(args.warmup):
+        pkv.kv_cache_copy_blocks(src, dst, k, v)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    REGIONS.resume()
+    for a, b in ev:
+        a.record()
+        pkv.kv_cache_copy_blocks(src, dst, k, v)
+        b.record()
+    torch.cuda.synchronize()
+    warm = back_to_back_us(torch, lambda: pkv.kv_cache_copy_blocks(src, dst, k, v), args.steps)
+    REGIONS.pause()
+    us = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
+    moved = 2 * 2 * pairs * 8 * 16 * 128 * 2           # K and V, read and written
+    res["copy_blocks: 256 Llama-shaped blocks"] = {"us_median_one_call": round(us, 2),
+                                                    "us_back_to_back": round(warm, 2), "bytes": moved,
+                                                    "GB/s_back_to_back": round(moved / (warm / 1e6) / 1e9, 1)}
+    return res
 
 
 def calibrate_copy(torch):
@@ -330,6 +470,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the smaller decode shapes and the block kernels")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (scale for rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -355,7 +496,7 @@ def main():
     case = d.pop("case")
     d.pop("pools")
     torch.cuda.empty_cache()
-    pre = None
+    pre = pre8 = None
     if not args.no_prefill:
         try:
             pre = bench_prefill(args, torch, pkv, workloads, tl)
@@ -363,6 +504,22 @@ def main():
                   flush=True)
         except pkv.PagedKVError as e:
             pre = {"error": str(e)}
+        torch.cuda.empty_cache()
+        try:
+            pre8 = bench_prefill(args, torch, pkv, workloads, tl, kv_dtype="i8")
+            print(f"[bench] prefill INT8: {pre8['us_per_call']:.1f} us = {pre8['roofline']['achieved']:.0f} TFLOP/s",
+                  flush=True)
+        except pkv.PagedKVError as e:
+            pre8 = {"error": str(e)}
+        torch.cuda.empty_cache()
+    shapes = blocks = None
+    if not args.no_extra:
+        shapes = bench_decode_shapes(args, torch, pkv, workloads, tl)
+        for k_, v_ in shapes.items():
+            b_ = v_["best_partition_size_cold"]
+            print(f"[bench] {k_}: best partition {b_}: {v_['by_partition_size'][b_]}", flush=True)
+        blocks = bench_block_ops(args, torch, pkv, workloads)
+        print(f"[bench] block ops: {blocks}", flush=True)
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (fp64 oracle, one thread)...", flush=True)
@@ -397,6 +554,9 @@ def main():
         "algorithmic_bytes": d["bytes"],
         "max_abs_err_sampled": d["max_abs_err"],
         "prefill": pre,
+        "prefill_int8": pre8,
+        "decode_shapes": shapes,
+        "block_ops": blocks,
     }
     print(json.dumps(line), flush=True)
 
