@@ -316,6 +316,80 @@ def bench_prefill(args, torch, pkv, workloads, tl, kv_dtype="bf16"):
             "max_abs_err": float(err)}
 
 
+# ------------------------------------------------------------------ mixed step
+def bench_mixed(args, torch, pkv, workloads, tl):
+    """A serving step mixing 16 prefill chunks (256 tokens each) with 240 decode
+    rows, window 4096: one prefill-kernel launch over the whole batch, against
+    two launches on the same pool (prefill kernel over the chunks, decode kernel
+    over the decode rows).  Sampled rows of both are checked against the oracle."""
+    dev = torch.device("cuda", 0)
+    case = workloads.mixed_step()
+    pools = tl.alloc_pools(case, dev)
+    tl.write_tokens(case, pools, dev, "all")
+    bt, lens, cu = tl.tables(case, dev)
+    q = case.q(dev)
+    npf = int((case.new_lens > 1).sum())
+    rows_pf = int(case.cu_q_lens[npf])
+    out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    out2 = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    ws = pkv.decode_workspace_size(case.num_seqs - npf, case.num_q_heads, case.head_dim, case.max_blocks_per_seq,
+                                   case.block_size, 512)
+    workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
+    cu_pf = cu[:npf + 1].contiguous()
+
+    def one():
+        pkv.paged_attention_prefill_chunk(q, cu, lens, pools["k"], pools["v"], bt, case.max_q_len,
+                                          case.softmax_scale, sliding_window=case.window, out=out)
+
+    def two():
+        pkv.paged_attention_prefill_chunk(q[:rows_pf], cu_pf, lens[:npf], pools["k"], pools["v"], bt[:npf],
+                                          case.max_q_len, case.softmax_scale, sliding_window=case.window,
+                                          out=out2[:rows_pf])
+        pkv.paged_attention_decode(q[rows_pf:], pools["k"], pools["v"], bt[npf:], lens[npf:], case.softmax_scale,
+                                   sliding_window=case.window, partition_size=512, out=out2[rows_pf:],
+                                   workspace=workspace)
+
+    res = {"workload": "mixed serving step: 16 prefill chunks of 256 tokens on 1024..16384-token contexts + "
+                       "240 decode rows on clipped log-normal contexts (median 2048), 32 q / 8 kv heads, "
+                       "head_dim 128, bf16, window 4096",
+           "algorithmic_flops": prefill_flops(case)}
+    for name, fn in (("one_launch_prefill_kernel", one), ("two_launches_prefill_plus_decode", two)):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        REGIONS.resume()
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        REGIONS.pause()
+        us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+        res[name] = {"us_per_step": round(us, 2), "TFLOP/s": round(res["algorithmic_flops"] / (us / 1e6) / 1e12, 1)}
+    # both paths against the oracle on sampled rows (decode over the matching prefix)
+    import oracle
+    from oracle.cases import build_cache, to_numpy
+    picks = [0, 9, 16, 100, case.num_seqs - 1]
+    sub = case.subset(picks)
+    cache = build_cache(sub, device=dev)
+    qs = to_numpy(sub.q(dev))
+    err = 0.0
+    for si, s_ in enumerate(picks):
+        L, C = int(case.seq_lens[s_]), int(case.new_lens[s_])
+        for i in sorted({0, C - 1}):
+            row = int(sub.cu_q_lens[si]) + i
+            ref = oracle.decode(cache, qs[row:row + 1], "bf16", np.array([L - C + i + 1], np.int32),
+                                sub.block_tables[si:si + 1], sub.softmax_scale, sub.window)
+            r = int(case.cu_q_lens[s_]) + i
+            err = max(err, tl.assert_close(out[r:r + 1], ref, "bf16", "mixed one launch"),
+                      tl.assert_close(out2[r:r + 1], ref, "bf16", "mixed two launches"))
+    res["max_abs_err_sampled"] = float(err)
+    del pools
+    torch.cuda.empty_cache()
+    return res
+
+
 # ------------------------------------------------------------------ other decode shapes
 def back_to_back_us(torch, fn, n):
     """GPU time per call of n calls queued back to back: the GPU is held by a
@@ -512,8 +586,10 @@ def main():
         except pkv.PagedKVError as e:
             pre8 = {"error": str(e)}
         torch.cuda.empty_cache()
-    shapes = blocks = None
+    shapes = blocks = mixed = None
     if not args.no_extra:
+        mixed = bench_mixed(args, torch, pkv, workloads, tl)
+        print(f"[bench] mixed step: {mixed}", flush=True)
         shapes = bench_decode_shapes(args, torch, pkv, workloads, tl)
         for k_, v_ in shapes.items():
             b_ = v_["best_partition_size_cold"]
@@ -555,6 +631,7 @@ def main():
         "max_abs_err_sampled": d["max_abs_err"],
         "prefill": pre,
         "prefill_int8": pre8,
+        "mixed_step": mixed,
         "decode_shapes": shapes,
         "block_ops": blocks,
     }

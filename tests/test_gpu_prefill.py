@@ -167,3 +167,37 @@ def test_int8_prefill_window_4096_full_size_sampled_rows():
             ref = oracle.decode(cache, q[row:row + 1], "bf16", np.array([L - C + i + 1], np.int32),
                                 sub.block_tables[si:si + 1], sub.softmax_scale, sub.window)
             assert_close(out[cu_full[s] + i:cu_full[s] + i + 1], ref, "bf16", f"int8 seq {s} row {i}")
+
+
+# ---------------------------------------------------------------- mixed batches
+@pytest.mark.parametrize("window", [0, 300])
+def test_mixed_decode_and_prefill_batch_in_one_launch(window):
+    """Decode rows (chunks of one token) and prefill chunks in the same launch
+    ("PyTorch LLM Serving Engine", What is implemented: prefill chunks share the
+    step with decode work)."""
+    lens = [900, 40, 1, 2000, 17, 333, 64, 1500, 250, 5]
+    new = [128, 1, 1, 1, 17, 1, 64, 200, 1, 1]
+    case = _case(lens, new, hq=12, hkv=2, window=window)
+    out, _ = _gpu(case)
+    assert_close(out, expected_outputs(case), "bf16", f"mixed W={window}")
+
+
+def test_mixed_step_full_size_sampled_rows():
+    """The mixed serving step at full size (16 chunks of 256 + 240 decode rows,
+    32 q / 8 kv heads, window 4096): sampled decode rows and chunk rows against
+    the oracle's decode over the matching prefix (pinned equal to chunk rows)."""
+    case = workloads.mixed_step()
+    out, _ = _gpu(case)
+    assert torch.isfinite(out).all()
+    picks = [0, 7, 15] + list(range(16, case.num_seqs, 9))
+    sub = case.subset(picks)
+    cache = build_cache(sub, device=device())
+    q = to_numpy(sub.q(device()))
+    cu = case.cu_q_lens
+    for si, s in enumerate(picks):
+        L, C = int(case.seq_lens[s]), int(case.new_lens[s])
+        for i in sorted({0, C - 1, C // 2}):
+            row = int(sub.cu_q_lens[si]) + i
+            ref = oracle.decode(cache, q[row:row + 1], "bf16", np.array([L - C + i + 1], np.int32),
+                                sub.block_tables[si:si + 1], sub.softmax_scale, sub.window)
+            assert_close(out[cu[s] + i:cu[s] + i + 1], ref, "bf16", f"seq {s} row {i}")

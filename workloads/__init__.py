@@ -433,10 +433,24 @@ def prefill_window(num_seqs: int = 16, chunk: int = 256, seed: int = 5) -> Paged
                      max_blocks=(16384 + chunk) // 16, window=4096, kind="prefill")
 
 
+def mixed_step(num_prefill: int = 16, chunk: int = 256, num_decode: int = 240, seed: int = 6) -> PagedCase:
+    """One serving step that mixes chunked prefill with decode: 16 sequences
+    appending a 256-token chunk to contexts of 1024..16384 tokens (uniform) and
+    240 sequences decoding one token after clipped log-normal contexts (median
+    2048, 128..32768), 32 q / 8 kv heads, head_dim 128, window 4096."""
+    ctx = uniform_ints(seed, num_prefill, 1024, 16384)
+    dec = lognormal_lengths(seed + 100, num_decode, 2048, 128, 32768)
+    lens = np.concatenate([ctx + chunk, dec]).astype(np.int32)
+    new = np.concatenate([np.full(num_prefill, chunk, np.int32), np.ones(num_decode, np.int32)])
+    return make_case("mixed-step", seed, lens, new, 32, 8, 128, max_blocks=32768 // 16, window=4096,
+                     kind="prefill")
+
+
 WORKLOADS = {
     "tiny-fp32-decode": tiny_fp32_decode,
     "qwen2.5-1.5b-decode": qwen_decode,
     "llama3-8b-decode": llama_decode,
     "int8-kv-decode": int8_decode,
     "prefill-window": prefill_window,
+    "mixed-step": mixed_step,
 }
