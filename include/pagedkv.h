@@ -141,10 +141,12 @@ size_t paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_q_hea
  *   workspace     device scratch of at least
  *                 paged_attention_decode_workspace_size(...) bytes, 256-byte
  *                 aligned; may be NULL when that size is 0.  Its contents need
- *                 no initialisation and are not preserved: the call clears its
- *                 work counter (first 256 bytes) with a kernel on `stream`
- *                 before use, so the call can be captured in a graph.  Two
- *                 calls in flight at once must not share a workspace.
+ *                 no initialisation and are not preserved: when the batch can
+ *                 hold more work items than the GPU runs at once, the call
+ *                 clears its work counter (first 256 bytes) with a kernel on
+ *                 `stream` before use (so the call can be captured in a
+ *                 graph); smaller batches use no counter.  Two calls in
+ *                 flight at once must not share a workspace.
  * num_seqs == 0 is a no-op.  out must not alias any input or the workspace.
  */
 int paged_attention_decode(const pkv_cache_desc* cache,

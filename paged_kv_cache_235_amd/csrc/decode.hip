@@ -11,7 +11,8 @@
 //    first turns the context lengths into a prefix of per-sequence partition
 //    counts in LDS; items 0 .. grid-1 go to the workgroups in order, later ones
 //    are claimed from a counter in the workspace (balanced, and the items in
-//    flight stay neighbours).  No host knowledge of the lengths is needed.
+//    flight stay neighbours).  No host knowledge of the lengths is needed.  A
+//    batch whose every possible item has a workgroup needs no counter.
 //  * Inside an item the 4 waves take the blocks round-robin.  Each wave streams
 //    its blocks' K and V tiles -- whole (block, KV head) runs, read with
 //    coalesced 16-byte loads -- as one sequence K0 V0 K1 V1 ..., each tile
@@ -793,10 +794,13 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
         b.context_lens = L.context_lens + s0;
         b.part_ml = merge ? ml_base + (int64_t)s0 * L.num_q_heads * max_parts * 2 : nullptr;
         b.part_o = merge ? o_base + (int64_t)s0 * L.num_q_heads * max_parts * L.head_dim : nullptr;
-        b.ticket = ticket;
+        // when every possible item has a workgroup of its own (a small batch), items
+        // go by stride and the counter -- and the launch that clears it -- is not needed
+        const bool claim = ticket && (int64_t)n * per_seq_items > resident;
+        b.ticket = claim ? ticket : nullptr;
         const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(resident, (int64_t)n * per_seq_items));
         hipError_t e = hipSuccess;
-        if (ticket) {
+        if (claim) {
             e = launch(decode_reset_kernel, dim3(1), dim3(kWave), 0, stream, ticket);
             if (e != hipSuccess) return e;
         }

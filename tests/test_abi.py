@@ -128,3 +128,62 @@ def test_prefill_validation(lib):
 
 def test_version(lib):
     assert b"gfx950" in lib.pkv_version()
+
+
+def test_slot_mapping_validation(lib):
+    f = lib.pkv_build_slot_mapping
+    d = _desc()
+    args = lambda **k: (ctypes.byref(k.get("desc", d)), k.get("cu", FAKE), k.get("b", 2), k.get("lens", FAKE),
+                        k.get("tables", FAKE), k.get("maxb", 4), k.get("out", FAKE), k.get("rows", 10), None)
+    assert f(*args(b=0)) == PKV_OK                       # nothing to do: no launch
+    assert f(*args(rows=0)) == PKV_OK
+    assert f(*args(b=-1)) == PKV_EINVAL
+    assert f(*args(rows=-5)) == PKV_EINVAL
+    assert f(*args(maxb=0)) == PKV_EINVAL
+    assert f(*args(cu=None)) == PKV_EINVAL
+    assert f(*args(out=None)) == PKV_EINVAL
+    assert f(*args(desc=_desc(bs=32))) == PKV_EUNSUPPORTED
+    assert f(None, FAKE, 2, FAKE, FAKE, 4, FAKE, 10, None) == PKV_EINVAL
+    assert lib.pkv_last_error()                          # the reason is reported
+
+
+def test_copy_blocks_validation(lib):
+    f = lib.kv_cache_copy_blocks
+    d = _desc()
+    d8 = _desc(dt=I8)
+    args = lambda **k: (ctypes.byref(k.get("desc", d)), k.get("k", FAKE), k.get("v", FAKE), k.get("ks"),
+                        k.get("vs"), k.get("src", FAKE), k.get("dst", FAKE), k.get("n", 3), None)
+    assert f(*args(n=0)) == PKV_OK
+    assert f(*args(n=-1)) == PKV_EINVAL
+    assert f(*args(src=None)) == PKV_EINVAL
+    assert f(*args(k=ctypes.c_void_p(0x1008))) == PKV_EINVAL          # pools 16-byte aligned
+    assert f(*args(ks=FAKE, vs=FAKE)) == PKV_EINVAL                    # no scales for bf16 pools
+    assert f(*args(desc=d8)) == PKV_EINVAL                             # INT8 needs both scale pools
+    assert f(*args(desc=d8, ks=FAKE)) == PKV_EINVAL
+    assert f(*args(desc=d8, ks=FAKE, vs=FAKE, n=0)) == PKV_OK
+    assert f(*args(desc=_desc(d=96))) == PKV_EUNSUPPORTED
+
+
+def test_allocator_abi_rejects_null_and_bad_sizes(lib):
+    P = ctypes.c_void_p
+    h = P()
+    assert lib.pkv_allocator_create(0, 16, ctypes.byref(h)) == PKV_EINVAL and not h.value
+    assert lib.pkv_allocator_create(4, 16, None) == PKV_EINVAL
+    assert lib.pkv_allocator_create(4, 16, ctypes.byref(h)) == PKV_OK and h.value
+    try:
+        assert lib.pkv_allocator_num_free(h) == 4
+        assert lib.pkv_allocator_num_free(None) == -1
+        assert lib.pkv_allocator_refcount(h, 4) == -1 and lib.pkv_allocator_refcount(h, -1) == -1
+        ids = (ctypes.c_int32 * 8)()
+        assert lib.pkv_allocator_alloc(h, 5, ids) == 5                 # PKV_ENOSPACE
+        assert lib.pkv_allocator_num_free(h) == 4
+        assert lib.pkv_allocator_alloc(h, -1, ids) == PKV_EINVAL
+        assert lib.pkv_allocator_alloc(h, 2, None) == PKV_EINVAL
+        n = ctypes.c_int32(0)
+        assert lib.pkv_seq_append(h, ids, 8, -1, 1, ids, ids, ctypes.byref(n)) == PKV_EINVAL
+        assert lib.pkv_seq_append(None, ids, 8, 0, 1, ids, ids, ctypes.byref(n)) == PKV_EINVAL
+        assert lib.pkv_seq_evict_window(h, ids, 10, 0, None) == PKV_EINVAL
+        assert lib.pkv_seq_truncate(h, ids, 3, 4) == PKV_EINVAL
+    finally:
+        assert lib.pkv_allocator_destroy(h) == PKV_OK
+    assert lib.pkv_allocator_destroy(None) == PKV_OK
