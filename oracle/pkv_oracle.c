@@ -319,12 +319,18 @@ static double pool_value(const void* pool, const uint16_t* scale, int32_t kv_dty
  * Token j of the sequence lives in physical block block_table[j / bs] at
  * offset j % bs ("MicroGen", Key Features: logical-to-physical mapping).
  */
-static void gather(const void* pool, const uint16_t* scale, int32_t kv_dtype,
+static void gather(const void* pool, const uint16_t* scale, int32_t kv_dtype, int32_t num_blocks,
                    int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
                    const int32_t* table_row, int32_t g, int32_t len, double* dst)
 {
     for (int32_t j = 0; j < len; ++j) {
         int64_t blk = table_row[j / block_size];
+        if (blk < 0 || blk >= num_blocks) {
+            /* no block (an entry released by window eviction): these keys are
+               outside every query's window; NaN makes any use of them show */
+            for (int32_t d = 0; d < head_dim; ++d) dst[(int64_t)j * head_dim + d] = NAN;
+            continue;
+        }
         int64_t vec = (blk * num_kv_heads + g) * block_size + j % block_size;
         for (int32_t d = 0; d < head_dim; ++d)
             dst[(int64_t)j * head_dim + d] = pool_value(pool, scale, kv_dtype, vec, head_dim, d);
@@ -418,8 +424,8 @@ int orc_attention(int32_t num_blocks, int32_t block_size, int32_t num_kv_heads, 
         if (!K || !V || !scores || !qv) { free(K); free(V); free(scores); free(qv); return 2; }
 
         for (int32_t g = 0; g < num_kv_heads; ++g) {
-            gather(k_pool, k_scale, kv_dtype, block_size, num_kv_heads, D, table_row, g, L, K);
-            gather(v_pool, v_scale, kv_dtype, block_size, num_kv_heads, D, table_row, g, L, V);
+            gather(k_pool, k_scale, kv_dtype, num_blocks, block_size, num_kv_heads, D, table_row, g, L, K);
+            gather(v_pool, v_scale, kv_dtype, num_blocks, block_size, num_kv_heads, D, table_row, g, L, V);
             for (int32_t i = 0; i < C; ++i) {
                 const int64_t row = (int64_t)r0 + i;
                 const int32_t p = L - C + i;
@@ -504,8 +510,8 @@ int orc_decode_split(int32_t num_blocks, int32_t block_size, int32_t num_kv_head
         double* ok = (double*)malloc(sizeof(double) * (size_t)D);
         if (!K || !V || !qv || !acc || !ok) { free(K); free(V); free(qv); free(acc); free(ok); return 2; }
         for (int32_t g = 0; g < num_kv_heads; ++g) {
-            gather(k_pool, k_scale, kv_dtype, block_size, num_kv_heads, D, table_row, g, L, K);
-            gather(v_pool, v_scale, kv_dtype, block_size, num_kv_heads, D, table_row, g, L, V);
+            gather(k_pool, k_scale, kv_dtype, num_blocks, block_size, num_kv_heads, D, table_row, g, L, K);
+            gather(v_pool, v_scale, kv_dtype, num_blocks, block_size, num_kv_heads, D, table_row, g, L, V);
             const int32_t p = L - 1;
             const int32_t lo = first_visible(p, window);
             for (int32_t h = g * G; h < (g + 1) * G; ++h) {

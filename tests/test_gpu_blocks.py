@@ -289,7 +289,8 @@ def test_window_eviction_changes_no_output_bit(window):
     assert len(freed) == sum(n_dec)
     m.append(2, m.alloc.num_free * BS)                  # takes every free block, the evicted ones included
     assert set(freed) <= set(m.rows[2].tolist())
-    dec1, _ = m.decode([0, 1], q, window=window)
-    pre1, _ = m.prefill([0, 1], chunk, qp, window=window)
+    dec1, dref1 = m.decode([0, 1], q, window=window)
+    pre1, pref1 = m.prefill([0, 1], chunk, qp, window=window)
     assert torch.equal(dec1, dec0)
     assert torch.equal(pre1, pre0)
+    assert np.array_equal(dref1, dref) and np.array_equal(pref1, pref)   # the oracle agrees

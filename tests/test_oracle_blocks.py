@@ -129,3 +129,29 @@ def test_copied_blocks_attend_identically():
     case.block_tables[2, :nblk] = dst
     got = expected_outputs(case, cache=cache)
     assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("kind", ["decode", "prefill"])
+def test_missing_blocks_before_the_window_change_nothing(kind):
+    """Window eviction releases the blocks wholly before every query's window and
+    marks their table entries -1 ("MicroGen", Key Features: window-length
+    eviction); the oracle must give the same output without reading them, and
+    NaN if a query could see such a block."""
+    W = 40
+    lens, new = [300, 97, 64], ([1, 1, 1] if kind == "decode" else [20, 30, 64])
+    case = workloads.make_case("evict", 64, lens, new, 8, 2, 64, window=W, kind=kind)
+    cache = build_cache(case)
+    ref = expected_outputs(case, cache=cache)
+    evicted = case.block_tables.copy()
+    for s in range(case.num_seqs):
+        first_query = int(case.seq_lens[s]) - int(case.new_lens[s])
+        dead = max(0, first_query - W + 1) // 16
+        evicted[s, :dead] = -1
+    assert (evicted == -1).any()
+    case.block_tables = evicted
+    assert np.array_equal(expected_outputs(case, cache=cache), ref)
+    # one more block, still inside a window: the output shows it
+    s = 0
+    first_query = int(case.seq_lens[s]) - int(case.new_lens[s])
+    evicted[s, max(0, first_query - W + 1) // 16] = -1
+    assert np.isnan(expected_outputs(case, cache=cache)[case.cu_q_lens[s]]).all()
