@@ -316,6 +316,60 @@ def bench_prefill(args, torch, pkv, workloads, tl, kv_dtype="bf16"):
             "max_abs_err": float(err)}
 
 
+# ------------------------------------------------------------------ INT8 at the large batch
+def bench_decode_int8_large(args, torch, pkv, workloads, tl):
+    """The Llama-3-8B-shaped decode batch over an INT8 pool (K/V written through
+    the quantising cache write): the partition kernel's time and its algorithmic
+    bytes (codes + fp16 scales) per second, next to the bf16 figure."""
+    import dataclasses
+    dev = torch.device("cuda", 0)
+    case = dataclasses.replace(workloads.llama_decode(), kv_dtype="i8")
+    pools = tl.alloc_pools(case, dev)
+    tl.write_tokens(case, pools, dev, "all")
+    bt, lens, _ = tl.tables(case, dev)
+    q = case.q(dev)
+    out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    ws = pkv.decode_workspace_size(case.num_seqs, case.num_q_heads, case.head_dim, case.max_blocks_per_seq,
+                                   case.block_size, case.partition_size)
+    workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+
+    def call(e=None):
+        if e:
+            pkv.set_decode_start_event(e[0])
+            pkv.set_decode_split_event(e[1])
+        pkv.paged_attention_decode(q, pools["k"], pools["v"], bt, lens, case.softmax_scale,
+                                   partition_size=case.partition_size, k_scale=pools["ks"], v_scale=pools["vs"],
+                                   out=out, workspace=workspace)
+        if e:
+            pkv.set_decode_start_event(None)
+            pkv.set_decode_split_event(None)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    REGIONS.resume()
+    for e in ev:
+        call(e)
+    torch.cuda.synchronize()
+    REGIONS.pause()
+    us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+    check = sorted({int(np.argmax(case.seq_lens)), int(np.argmin(case.seq_lens)), 7})
+    sub = case.subset(check)
+    from oracle.cases import build_cache, expected_outputs
+    err = tl.assert_close(out[check], expected_outputs(sub, cache=build_cache(sub, device=dev)), "bf16",
+                          "int8 large decode")
+    b = decode_bytes(case)
+    part_bytes = b["kv"] + b["table"] + b["q"]
+    del pools
+    torch.cuda.empty_cache()
+    return {"workload": "Llama-3-8B-shaped decode batch (256 seqs, 840,545 tokens) over an INT8 pool",
+            "partition_us": round(us, 1), "algorithmic_bytes_per_launch": part_bytes,
+            "GB/s": round(part_bytes / (us / 1e6) / 1e9, 1),
+            "frac_of_hbm_peak": round(part_bytes / (us / 1e6) / 1e9 / HBM_PEAK_GBS, 4),
+            "max_abs_err_sampled": float(err)}
+
+
 # ------------------------------------------------------------------ mixed step
 def bench_mixed(args, torch, pkv, workloads, tl):
     """A serving step mixing 16 prefill chunks (256 tokens each) with 240 decode
@@ -586,8 +640,10 @@ def main():
         except pkv.PagedKVError as e:
             pre8 = {"error": str(e)}
         torch.cuda.empty_cache()
-    shapes = blocks = mixed = None
+    shapes = blocks = mixed = i8big = None
     if not args.no_extra:
+        i8big = bench_decode_int8_large(args, torch, pkv, workloads, tl)
+        print(f"[bench] INT8 Llama-shaped decode: {i8big}", flush=True)
         mixed = bench_mixed(args, torch, pkv, workloads, tl)
         print(f"[bench] mixed step: {mixed}", flush=True)
         shapes = bench_decode_shapes(args, torch, pkv, workloads, tl)
@@ -631,6 +687,7 @@ def main():
         "max_abs_err_sampled": d["max_abs_err"],
         "prefill": pre,
         "prefill_int8": pre8,
+        "decode_int8_llama_shaped": i8big,
         "mixed_step": mixed,
         "decode_shapes": shapes,
         "block_ops": blocks,
