@@ -66,6 +66,8 @@ template <int KV> struct KvT;
 template <> struct KvT<KV_F32> { static constexpr int ESZ = 4, LW = 16; };
 template <> struct KvT<KV_BF16> { static constexpr int ESZ = 2, LW = 16; };
 template <> struct KvT<KV_I8> { static constexpr int ESZ = 1, LW = 8; };
+template <> struct KvT<KV_I8Q> { static constexpr int ESZ = 1, LW = 8; };
+constexpr bool is_i8(int kv) { return kv == KV_I8 || kv == KV_I8Q; }
 
 template <int KV, int D, int GT>
 struct Cfg {
@@ -156,7 +158,7 @@ __device__ __forceinline__ void load_tile(Tile<KV, D, GT>& t, const char* pool, 
     const char* p = pool + tile * C::TILE_BYTES;
 #pragma unroll
     for (int i = 0; i < C::NLOAD; ++i) t.w[i] = load_words<C::WORDS>(p + (i * kWave + lane) * C::LW);
-    if constexpr (KV == KV_I8) {
+    if constexpr (is_i8(KV)) {
 #pragma unroll
         for (int i = 0; i < C::NLOAD; ++i)
             t.sc[i] = (float)__builtin_bit_cast(_Float16, scales[tile * kBlk + i * C::RPL + lane / C::LPR]);
@@ -263,7 +265,8 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
 
     // query fragment: this lane's columns of each head
     uint32_t qw[GT][C::WORDS];      // bf16 pairs (bf16 pools)
-    float qf[GT][C::EPL];           // fp32 (fp32 and INT8 pools)
+    uint32_t qb[GT][C::EPL / 2];    // bf16 pairs (INT8 pools with a bf16 query)
+    float qf[GT][C::EPL];           // fp32 (fp32 pools, INT8 pools with an fp32 query)
     float qsum[GT];
     auto load_q = [&](const Item& I) {
 #pragma unroll
@@ -278,6 +281,14 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
                 }
 #pragma unroll
                 for (int i = 0; i < C::WORDS; ++i) qw[j][i] = t.w[i];
+            } else if constexpr (KV == KV_I8Q) {
+                u32x4_t v = {0u, 0u, 0u, 0u};
+                if (j < I.nh) v = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.q) + qoff);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    qb[j][i] = v[i];
+                    qsum[j] += bf16lo(v[i]) + bf16hi(v[i]);
+                }
             } else {
 #pragma unroll
                 for (int e = 0; e < C::EPL; ++e) {
@@ -418,6 +429,29 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
                                                                     __builtin_bit_cast(bf16x2_t, qw[j][w]), d, false);
                             part[i * GT + j] = d;
                         }
+                    } else if constexpr (KV == KV_I8Q) {
+                        // the 8 biased codes u = q8 + 128 as 4 bf16 pairs (small
+                        // integers: exact), then the bf16 path's dot2 products
+                        uint32_t cw[4];
+#pragma unroll
+                        for (int w = 0; w < 2; ++w) {
+                            const uint32_t u = t.w[i].w[w] ^ 0x80808080u;
+                            const float f0 = (float)(u & 0xffu), f1 = (float)((u >> 8) & 0xffu);
+                            const float f2 = (float)((u >> 16) & 0xffu), f3 = (float)(u >> 24);
+                            cw[2 * w] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, f1),
+                                                              __builtin_bit_cast(uint32_t, f0), 0x07060302u);
+                            cw[2 * w + 1] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, f3),
+                                                                  __builtin_bit_cast(uint32_t, f2), 0x07060302u);
+                        }
+#pragma unroll
+                        for (int j = 0; j < GT; ++j) {
+                            float d = 0.0f;
+#pragma unroll
+                            for (int w = 0; w < 4; ++w)
+                                d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, cw[w]),
+                                                                    __builtin_bit_cast(bf16x2_t, qb[j][w]), d, false);
+                            part[i * GT + j] = (d - 128.0f * qsum[j]) * t.sc[i];
+                        }
                     } else {
                         float x[C::EPL];
                         widen<KV, C::WORDS>(t.w[i], x);
@@ -503,7 +537,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
                         const f32x4_t p1 = *reinterpret_cast<const f32x4_t*>(pp + 4);
                         p[4] = p1[0]; p[5] = p1[1]; p[6] = p1[2]; p[7] = p1[3];
                     }
-                    if constexpr (KV == KV_I8) {
+                    if constexpr (is_i8(KV)) {
 #pragma unroll
                         for (int j = 0; j < GT; ++j) {
                             p[j] = row_ok ? p[j] * t.sc[i] : 0.0f;
@@ -557,7 +591,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
                 if (kk < tb_valid && (tb_base + kk) % GT == j) v += l_lane[kk];
             l_run[j] = group_sum<kWave>(v);
         }
-        if constexpr (KV == KV_I8) {
+        if constexpr (is_i8(KV)) {
 #pragma unroll
             for (int j = 0; j < GT; ++j)
 #pragma unroll
@@ -719,6 +753,7 @@ static PartKernel pick_gt(int gt) {
 static PartKernel pick(KvKind kv, int D, int gt) {
     if (kv == KV_F32) return D == 64 ? pick_gt<KV_F32, 64>(gt) : pick_gt<KV_F32, 128>(gt);
     if (kv == KV_BF16) return D == 64 ? pick_gt<KV_BF16, 64>(gt) : pick_gt<KV_BF16, 128>(gt);
+    if (kv == KV_I8Q) return D == 64 ? pick_gt<KV_I8Q, 64>(gt) : pick_gt<KV_I8Q, 128>(gt);
     return D == 64 ? pick_gt<KV_I8, 64>(gt) : pick_gt<KV_I8, 128>(gt);
 }
 

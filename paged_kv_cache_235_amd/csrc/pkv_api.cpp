@@ -282,7 +282,8 @@ int paged_attention_decode(const pkv_cache_desc* cache, const void* q, int32_t q
     L.head_dim = cache->head_dim;
     L.block_size = cache->block_size;
     L.num_blocks = cache->num_blocks;
-    L.kv = kv == PKV_F32 ? pkv::KV_F32 : kv == PKV_BF16 ? pkv::KV_BF16 : pkv::KV_I8;
+    L.kv = kv == PKV_F32 ? pkv::KV_F32 : kv == PKV_BF16 ? pkv::KV_BF16
+                                          : (q_dtype == PKV_BF16 ? pkv::KV_I8Q : pkv::KV_I8);
     L.k_pool = k_pool;
     L.v_pool = v_pool;
     L.k_scale = static_cast<const uint16_t*>(k_scale);

@@ -41,7 +41,8 @@ struct KvWriteLaunch {
 };
 hipError_t launch_kv_write(const KvWriteLaunch& L, hipStream_t stream);
 
-enum KvKind { KV_F32 = 0, KV_BF16 = 1, KV_I8 = 2 };
+// KV_I8Q: an INT8 pool read with a bf16 query (Q.K^T by bf16 dot products of the codes)
+enum KvKind { KV_F32 = 0, KV_BF16 = 1, KV_I8 = 2, KV_I8Q = 3 };
 
 struct DecodeLaunch {
     const void* q;
