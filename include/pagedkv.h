@@ -307,6 +307,7 @@ int pkv_seq_fork(pkv_block_allocator* a, const int32_t* parent_row, int32_t len,
  * from ceil(new_len / block_size) to ceil(len / block_size) are released and
  * set to -1.  Positions >= new_len inside the kept last block are simply
  * overwritten by the next append.  Also frees a whole sequence (new_len 0).
+ * table_row must hold at least ceil(len / block_size) entries.
  */
 int pkv_seq_truncate(pkv_block_allocator* a, int32_t* table_row, int32_t len, int32_t new_len);
 
@@ -318,7 +319,8 @@ int pkv_seq_truncate(pkv_block_allocator* a, int32_t* table_row, int32_t len, in
  * released and set to -1; *num_released (may be NULL) counts the entries
  * released by this call.  The attention calls never read an entry before the
  * window, and treat an entry of -1 as no keys, so their results are unchanged
- * as long as they run with the same window.
+ * as long as they run with the same window.  table_row must hold at least
+ * ceil(len / block_size) entries.
  */
 int pkv_seq_evict_window(pkv_block_allocator* a, int32_t* table_row, int32_t len, int32_t window,
                          int32_t* num_released);
