@@ -172,12 +172,30 @@ class Cache:
         _check(rc, "kv_write")
 
 
-def slot_mapping(num_blocks, block_size, cu_q_lens, seq_lens, block_tables) -> np.ndarray:
+def logical_tables(block_tables, table_offsets=None) -> np.ndarray:
+    """The logical block table of offset rows ("MicroGen", Key Features: window
+    eviction): column c of row s holds logical block c + table_offsets[s], so
+    logical entry b is row[b - offset] and the blocks before the offset (released)
+    are -1.  Without offsets the table is its own logical table."""
+    tables = _c(block_tables, np.int32)
+    if table_offsets is None:
+        return tables
+    off = _c(table_offsets, np.int32)
+    if tables.ndim != 2 or off.shape != (tables.shape[0],) or (off < 0).any():
+        raise ValueError("table_offsets must be non-negative int32 [num_seqs]")
+    width = tables.shape[1] + (int(off.max()) if off.size else 0)
+    out = np.full((tables.shape[0], max(width, 1)), -1, np.int32)
+    for s in range(tables.shape[0]):
+        out[s, off[s]:off[s] + tables.shape[1]] = tables[s]
+    return out
+
+
+def slot_mapping(num_blocks, block_size, cu_q_lens, seq_lens, block_tables, table_offsets=None) -> np.ndarray:
     """Reference slot of every new row: row i of sequence s sits at position
     seq_lens[s] - C_s + i; -1 where the table holds no valid block."""
     cu = _c(cu_q_lens, np.int32)
     lens = _c(seq_lens, np.int32)
-    tables = _c(block_tables, np.int32)
+    tables = logical_tables(block_tables, table_offsets)
     out = np.empty(int(cu[-1]) if cu.size else 0, np.int32)
     rc = lib().orc_slot_mapping(num_blocks, block_size, lens.size, _ptr(cu), _ptr(lens), _ptr(tables),
                                 tables.shape[1] if tables.ndim == 2 else 0, _ptr(out))
@@ -197,13 +215,13 @@ def copy_blocks(cache: "Cache", src, dst) -> None:
 
 
 def attention(cache: Cache, q, q_dtype, cu_q_lens, seq_lens, block_tables, softmax_scale,
-              window=0, weights=False):
+              window=0, weights=False, table_offsets=None):
     """Reference attention for all query rows; returns out [rows][Hq][D] (and weights)."""
     q_dtype = DTYPES[q_dtype] if isinstance(q_dtype, str) else q_dtype
     q = _c(q, NP_TYPES[q_dtype])
     cu = _c(cu_q_lens, np.int32)
     lens = _c(seq_lens, np.int32)
-    tables = _c(block_tables, np.int32)
+    tables = logical_tables(block_tables, table_offsets)
     rows, hq, d = q.shape
     out = np.zeros((rows, hq, d), np.float64)
     wstride = int(lens.max()) if lens.size else 0
@@ -217,12 +235,12 @@ def attention(cache: Cache, q, q_dtype, cu_q_lens, seq_lens, block_tables, softm
 
 
 def decode(cache: Cache, q, q_dtype, context_lens, block_tables, softmax_scale, window=0,
-           weights=False):
+           weights=False, table_offsets=None):
     """Reference decode: one query per sequence at position context_lens[s] - 1."""
     q_dtype = DTYPES[q_dtype] if isinstance(q_dtype, str) else q_dtype
     q = _c(q, NP_TYPES[q_dtype])
     lens = _c(context_lens, np.int32)
-    tables = _c(block_tables, np.int32)
+    tables = logical_tables(block_tables, table_offsets)
     b, hq, d = q.shape
     out = np.zeros((b, hq, d), np.float64)
     wstride = max(int(lens.max()) if lens.size else 1, 1)

@@ -155,3 +155,49 @@ def test_missing_blocks_before_the_window_change_nothing(kind):
     first_query = int(case.seq_lens[s]) - int(case.new_lens[s])
     evicted[s, max(0, first_query - W + 1) // 16] = -1
     assert np.isnan(expected_outputs(case, cache=cache)[case.cu_q_lens[s]]).all()
+
+
+def test_logical_tables_of_offset_rows():
+    rows = np.array([[5, 6, 7], [9, -1, 3]], np.int32)
+    got = oracle.logical_tables(rows, np.array([2, 0], np.int32))
+    assert np.array_equal(got, [[-1, -1, 5, 6, 7], [9, -1, 3, -1, -1]])
+    assert np.array_equal(oracle.logical_tables(rows), rows)
+
+
+def _compact(case, W):
+    """Offset rows: drop each sequence's blocks wholly before its first query's
+    window; the narrower rows are padded with an id that is never read."""
+    offs, rows = [], []
+    for s in range(case.num_seqs):
+        first_query = int(case.seq_lens[s]) - int(case.new_lens[s])
+        offs.append(max(0, first_query - W + 1) // 16)
+        nblk = -(-int(case.seq_lens[s]) // 16)
+        rows.append(case.block_tables[s, offs[-1]:nblk])
+    width = max(len(r) for r in rows)
+    out = np.full((case.num_seqs, width), 7777, np.int32)
+    for s, r in enumerate(rows):
+        out[s, :len(r)] = r
+    return out, np.array(offs, np.int32)
+
+
+@pytest.mark.parametrize("kind", ["decode", "prefill"])
+def test_offset_tables_give_the_same_attention_and_slots(kind):
+    """A row whose column c holds logical block c + offset ("MicroGen", Key
+    Features: window eviction; the table keeps only the window's blocks)."""
+    W = 48
+    lens, new = [700, 97, 64, 300], ([1, 1, 1, 1] if kind == "decode" else [20, 30, 64, 5])
+    case = workloads.make_case("offset", 65, lens, new, 8, 2, 64, window=W, kind=kind)
+    cache = build_cache(case)
+    ref = expected_outputs(case, cache=cache)
+    rows, offs = _compact(case, W)
+    assert offs.max() > 0 and rows.shape[1] < case.block_tables.shape[1]
+    q = to_numpy(case.q())
+    if kind == "decode":
+        got = oracle.decode(cache, q, case.in_dtype, case.seq_lens, rows, case.softmax_scale, W, table_offsets=offs)
+    else:
+        got = oracle.attention(cache, q, case.in_dtype, case.cu_q_lens, case.seq_lens, rows, case.softmax_scale, W,
+                               table_offsets=offs)
+    assert np.array_equal(got, ref)
+    a = oracle.slot_mapping(case.num_blocks, 16, case.cu_q_lens, case.seq_lens, case.block_tables)
+    b = oracle.slot_mapping(case.num_blocks, 16, case.cu_q_lens, case.seq_lens, rows, table_offsets=offs)
+    assert np.array_equal(a, b)
