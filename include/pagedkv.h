@@ -105,12 +105,15 @@ int kv_cache_write(const pkv_cache_desc* cache,
 
 /*
  * Bytes of workspace paged_attention_decode needs for these sizes.  Zero when
- * partition_size is 0 (single pass) or covers max_blocks_per_seq*block_size.
- * Returns 0 for invalid sizes (the decode call then reports the error).
+ * partition_size is 0 (single pass) or one partition covers every key a row
+ * can address.  with_table_offsets: nonzero if the call passes table_offsets
+ * (a row's keys may then straddle one more partition).  Returns 0 for invalid
+ * sizes (the decode call then reports the error).
  */
 size_t paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
                                              int32_t head_dim, int32_t max_blocks_per_seq,
-                                             int32_t block_size, int32_t partition_size);
+                                             int32_t block_size, int32_t partition_size,
+                                             int32_t with_table_offsets);
 
 /*
  * paged_attention_decode -- one query token per sequence.
@@ -133,6 +136,13 @@ size_t paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_q_hea
  *                 entries past ceil(L / block_size) are never read, and with a
  *                 window neither are entries wholly before it (they may be -1
  *                 after pkv_seq_evict_window).
+ *   table_offsets NULL, or [num_seqs] int32 >= 0: column c of row s holds
+ *                 logical block c + table_offsets[s], so a windowed sequence's
+ *                 row can drop its released blocks (pkv_seq_compact) and stay
+ *                 max_blocks_per_seq wide however long the context grows.
+ *                 Keys of blocks before the offset do not exist for the call:
+ *                 the window must exclude them.  L is clamped to
+ *                 (max_blocks_per_seq + offset) * block_size.
  *   context_lens  [num_seqs] int32.
  *   partition_size  0: each sequence in one pass.  Otherwise a positive
  *                 multiple of block_size: contexts are split into partitions
@@ -156,6 +166,7 @@ int paged_attention_decode(const pkv_cache_desc* cache,
                            const void* k_pool, const void* v_pool,
                            const void* k_scale, const void* v_scale,
                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* table_offsets,
                            const int32_t* context_lens,
                            float softmax_scale, int32_t sliding_window,
                            int32_t partition_size,
@@ -183,6 +194,7 @@ int paged_attention_decode(const pkv_cache_desc* cache,
  *   block_tables  as for decode; with a window, entries wholly before the
  *                 first row's window may be -1 (evicted): they hold no key
  *                 any row can see.
+ *   table_offsets NULL, or per-sequence offsets as for decode.
  *   k_scale/v_scale  INT8 pools only (16-byte aligned), else NULL.
  * Pools are BF16 or INT8 ("MicroGen", Key Features: dynamic per-vector INT8
  * KV).  INT8 keys enter the scores exactly (code . q times the key's scale);
@@ -199,6 +211,7 @@ int paged_attention_prefill_chunk(const pkv_cache_desc* cache,
                                   const void* k_pool, const void* v_pool,
                                   const void* k_scale, const void* v_scale,
                                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* table_offsets,
                                   const int32_t* seq_lens,
                                   float softmax_scale, int32_t sliding_window,
                                   void* stream);
@@ -213,9 +226,10 @@ int paged_attention_prefill_chunk(const pkv_cache_desc* cache,
  * Sequence s owns rows [cu_q_lens[s], cu_q_lens[s+1]) (C_s of them: 1 for a
  * decode step, the chunk length for prefill) and holds L_s = seq_lens[s]
  * tokens once they are written, so row i sits at position p = L_s - C_s + i:
- *     slot_mapping[row] = block_tables[s][p / block_size] * block_size + p % block_size
- * or -1 (kv_cache_write then skips the row) when p < 0, p / block_size >=
- * max_blocks_per_seq, or the table entry is outside [0, num_blocks).
+ *     slot_mapping[row] = block_tables[s][p / block_size - o_s] * block_size + p % block_size
+ * with o_s = table_offsets[s] (0 when table_offsets is NULL), or -1
+ * (kv_cache_write then skips the row) when p < 0, the column is outside
+ * [0, max_blocks_per_seq), or the table entry is outside [0, num_blocks).
  *
  *   cu_q_lens     [num_seqs + 1] int32 prefix sums, cu_q_lens[0] == 0.
  *   seq_lens      [num_seqs] int32.
@@ -228,7 +242,8 @@ int paged_attention_prefill_chunk(const pkv_cache_desc* cache,
  */
 int pkv_build_slot_mapping(const pkv_cache_desc* cache, const int32_t* cu_q_lens, int32_t num_seqs,
                            const int32_t* seq_lens, const int32_t* block_tables, int32_t max_blocks_per_seq,
-                           int32_t* slot_mapping, int32_t total_rows, void* stream);
+                           const int32_t* table_offsets, int32_t* slot_mapping, int32_t total_rows,
+                           void* stream);
 
 /*
  * kv_cache_copy_blocks -- copy whole physical blocks: for each pair n, block
@@ -324,6 +339,18 @@ int pkv_seq_truncate(pkv_block_allocator* a, int32_t* table_row, int32_t len, in
  */
 int pkv_seq_evict_window(pkv_block_allocator* a, int32_t* table_row, int32_t len, int32_t window,
                          int32_t* num_released);
+
+/*
+ * pkv_seq_compact -- drop the released (-1) entries at the start of a table row
+ * and add their count to the row's offset (*table_offset; 0 for a row that
+ * starts at logical block 0), so a windowed sequence keeps a row of bounded
+ * width however long it grows; the attention calls and
+ * pkv_build_slot_mapping take the offsets as table_offsets.  A row of only
+ * -1 entries is left as it is.  The pkv_seq_* calls above work on an offset
+ * row when given lengths minus offset * block_size (they address the row's
+ * columns).  Host memory only; no allocator state is touched.
+ */
+int pkv_seq_compact(int32_t* table_row, int32_t max_blocks_per_seq, int32_t* table_offset);
 
 /* Text for the last non-OK status returned on this thread ("" if none). */
 const char* pkv_last_error(void);

@@ -28,7 +28,7 @@ EXPORTS = ("kv_cache_write", "paged_attention_decode_workspace_size", "paged_att
            "pkv_build_slot_mapping", "kv_cache_copy_blocks", "pkv_allocator_create", "pkv_allocator_destroy",
            "pkv_allocator_num_free", "pkv_allocator_refcount", "pkv_allocator_alloc", "pkv_allocator_retain",
            "pkv_allocator_release", "pkv_seq_append", "pkv_seq_fork", "pkv_seq_truncate",
-           "pkv_seq_evict_window")
+           "pkv_seq_evict_window", "pkv_seq_compact")
 
 
 class PagedKVError(RuntimeError):
@@ -61,13 +61,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.kv_cache_write.restype = ctypes.c_int
             lib.kv_cache_write.argtypes = [D, P, P, i32, i64, P, i32, P, P, P, P, P]
             lib.paged_attention_decode_workspace_size.restype = ctypes.c_size_t
-            lib.paged_attention_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+            lib.paged_attention_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
             lib.paged_attention_decode.restype = ctypes.c_int
-            lib.paged_attention_decode.argtypes = [D, P, i32, P, i32, i32, i32, P, P, P, P, P, i32, P,
+            lib.paged_attention_decode.argtypes = [D, P, i32, P, i32, i32, i32, P, P, P, P, P, i32, P, P,
                                                    f32, i32, i32, P, ctypes.c_size_t, P]
             lib.paged_attention_prefill_chunk.restype = ctypes.c_int
             lib.paged_attention_prefill_chunk.argtypes = [D, P, i32, P, i32, P, i32, i32, i32, P, P, P, P, P,
-                                                          i32, P, f32, i32, P]
+                                                          i32, P, P, f32, i32, P]
             lib.pkv_last_error.restype = ctypes.c_char_p
             lib.pkv_last_error.argtypes = []
             lib.pkv_version.restype = ctypes.c_char_p
@@ -77,7 +77,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.pkv_profile_set_decode_start_event.restype = ctypes.c_int
             lib.pkv_profile_set_decode_start_event.argtypes = [P]
             lib.pkv_build_slot_mapping.restype = ctypes.c_int
-            lib.pkv_build_slot_mapping.argtypes = [D, P, i32, P, P, i32, P, i32, P]
+            lib.pkv_build_slot_mapping.argtypes = [D, P, i32, P, P, i32, P, P, i32, P]
             lib.kv_cache_copy_blocks.restype = ctypes.c_int
             lib.kv_cache_copy_blocks.argtypes = [D, P, P, P, P, P, P, i32, P]
             lib.pkv_allocator_create.restype = ctypes.c_int
@@ -102,6 +102,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.pkv_seq_truncate.argtypes = [P, P, i32, i32]
             lib.pkv_seq_evict_window.restype = ctypes.c_int
             lib.pkv_seq_evict_window.argtypes = [P, P, i32, i32, P]
+            lib.pkv_seq_compact.restype = ctypes.c_int
+            lib.pkv_seq_compact.argtypes = [P, i32, P]
             _lib = lib
     return _lib
 
@@ -189,9 +191,18 @@ def kv_cache_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
 
 
 def decode_workspace_size(num_seqs: int, num_q_heads: int, head_dim: int, max_blocks_per_seq: int,
-                          block_size: int = 16, partition_size: int = 512) -> int:
+                          block_size: int = 16, partition_size: int = 512, with_table_offsets: bool = False) -> int:
     return int(load_library().paged_attention_decode_workspace_size(
-        num_seqs, num_q_heads, head_dim, max_blocks_per_seq, block_size, partition_size))
+        num_seqs, num_q_heads, head_dim, max_blocks_per_seq, block_size, partition_size, int(bool(with_table_offsets))))
+
+
+def _offsets(t, b, what="table_offsets"):
+    if t is None:
+        return None
+    if t.dtype != torch.int32 or t.shape != (b,):
+        raise ValueError(f"{what} must be int32 [num_seqs]")
+    _contig(t, what)
+    return t
 
 
 def paged_attention_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
@@ -199,9 +210,10 @@ def paged_attention_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.
                            sliding_window: int = 0, partition_size: int = 512,
                            k_scale: torch.Tensor | None = None, v_scale: torch.Tensor | None = None,
                            out: torch.Tensor | None = None, out_dtype: torch.dtype = torch.float32,
-                           workspace: torch.Tensor | None = None) -> torch.Tensor:
+                           workspace: torch.Tensor | None = None,
+                           table_offsets: torch.Tensor | None = None) -> torch.Tensor:
     """Decode attention for q [num_seqs][Hq][D]; returns out [num_seqs][Hq][D]."""
-    dev = _on_gpu(q, k_pool, v_pool, block_tables, context_lens, k_scale, v_scale, out, workspace)
+    dev = _on_gpu(q, k_pool, v_pool, block_tables, context_lens, k_scale, v_scale, out, workspace, table_offsets)
     _check_pools(k_pool, v_pool, k_scale, v_scale)
     desc = cache_desc(k_pool)
     _contig(q, "q")
@@ -220,13 +232,14 @@ def paged_attention_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.
         raise ValueError("out must have q's shape")
     _contig(out, "out")
     maxb = max(block_tables.shape[1], 1)
-    need = decode_workspace_size(b, hq, d, maxb, desc.block_size, partition_size) if b else 0
+    table_offsets = _offsets(table_offsets, b)
+    need = decode_workspace_size(b, hq, d, maxb, desc.block_size, partition_size, table_offsets is not None) if b else 0
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     lib = load_library()
     _check(lib.paged_attention_decode(
         ctypes.byref(desc), _ptr(q), _dtype(q, "q"), _ptr(out), _dtype(out, "out"), b, hq, _ptr(k_pool),
-        _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), maxb, _ptr(context_lens),
+        _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), maxb, _ptr(table_offsets), _ptr(context_lens),
         float(softmax_scale), int(sliding_window), int(partition_size), _ptr(workspace) if need else None,
         need, _stream(dev)))
     return out
@@ -238,9 +251,10 @@ def paged_attention_prefill_chunk(q: torch.Tensor, cu_q_lens: torch.Tensor, seq_
                                   out: torch.Tensor | None = None,
                                   out_dtype: torch.dtype = torch.float32,
                                   k_scale: torch.Tensor | None = None,
-                                  v_scale: torch.Tensor | None = None) -> torch.Tensor:
+                                  v_scale: torch.Tensor | None = None,
+                                  table_offsets: torch.Tensor | None = None) -> torch.Tensor:
     """Chunked-prefill attention for q [total_rows][Hq][D] (bf16) over bf16 or INT8 pools."""
-    dev = _on_gpu(q, cu_q_lens, seq_lens, k_pool, v_pool, block_tables, out, k_scale, v_scale)
+    dev = _on_gpu(q, cu_q_lens, seq_lens, k_pool, v_pool, block_tables, out, k_scale, v_scale, table_offsets)
     _check_pools(k_pool, v_pool, k_scale, v_scale)
     desc = cache_desc(k_pool)
     _contig(q, "q")
@@ -264,13 +278,14 @@ def paged_attention_prefill_chunk(q: torch.Tensor, cu_q_lens: torch.Tensor, seq_
     _check(lib.paged_attention_prefill_chunk(
         ctypes.byref(desc), _ptr(q), _dtype(q, "q"), _ptr(out), _dtype(out, "out"), _ptr(cu_q_lens), b,
         int(max_q_len), q.shape[1], _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
-        max(block_tables.shape[1], 1), _ptr(seq_lens), float(softmax_scale), int(sliding_window), _stream(dev)))
+        max(block_tables.shape[1], 1), _ptr(_offsets(table_offsets, b)), _ptr(seq_lens), float(softmax_scale),
+        int(sliding_window), _stream(dev)))
     return out
 
 
 def build_slot_mapping(cu_q_lens: torch.Tensor, seq_lens: torch.Tensor, block_tables: torch.Tensor,
                        k_pool: torch.Tensor, out: torch.Tensor | None = None,
-                       total_rows: int | None = None) -> torch.Tensor:
+                       total_rows: int | None = None, table_offsets: torch.Tensor | None = None) -> torch.Tensor:
     """Slot of every new row (row i of sequence s at position seq_lens[s] - C_s + i),
     computed on the GPU from the block tables; -1 where the table holds no block."""
     dev = _on_gpu(cu_q_lens, seq_lens, block_tables, out)
@@ -291,7 +306,8 @@ def build_slot_mapping(cu_q_lens: torch.Tensor, seq_lens: torch.Tensor, block_ta
     _contig(out, "out")
     lib = load_library()
     _check(lib.pkv_build_slot_mapping(ctypes.byref(desc), _ptr(cu_q_lens), b, _ptr(seq_lens), _ptr(block_tables),
-                                      max(block_tables.shape[1], 1), _ptr(out), out.shape[0], _stream(dev)))
+                                      max(block_tables.shape[1], 1), _ptr(_offsets(table_offsets, b)), _ptr(out),
+                                      out.shape[0], _stream(dev)))
     return out
 
 
@@ -390,6 +406,14 @@ class BlockAllocator:
     def truncate(self, row, length: int, new_length: int):
         row = _row(row, "row")
         _check(self._lib.pkv_seq_truncate(self._h, _np_ptr(row), int(length), int(new_length)))
+
+    @staticmethod
+    def compact(row, offset: int) -> int:
+        """Drop the row's leading released entries; returns the new offset."""
+        row = _row(row, "row")
+        off = ctypes.c_int32(int(offset))
+        _check(load_library().pkv_seq_compact(_np_ptr(row), row.size, ctypes.byref(off)))
+        return int(off.value)
 
     def evict_window(self, row, length: int, window: int) -> int:
         row = _row(row, "row")

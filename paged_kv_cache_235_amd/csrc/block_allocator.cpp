@@ -214,4 +214,18 @@ int pkv_seq_evict_window(pkv_block_allocator* a, int32_t* table_row, int32_t len
     return PKV_OK;
 }
 
+int pkv_seq_compact(int32_t* table_row, int32_t max_blocks_per_seq, int32_t* table_offset) {
+    pkv::clear_error();
+    if (!table_row || !table_offset) return report(PKV_EINVAL, "NULL argument");
+    if (max_blocks_per_seq < 0 || *table_offset < 0) return report(PKV_EINVAL, "negative size or offset");
+    int32_t n = 0;
+    while (n < max_blocks_per_seq && table_row[n] < 0) ++n;
+    if (n == max_blocks_per_seq) return PKV_OK;        // nothing held: leave the row as it is
+    if ((int64_t)*table_offset + n > INT32_MAX / 16) return report(PKV_EINVAL, "offset overflows");
+    for (int32_t i = n; i < max_blocks_per_seq; ++i) table_row[i - n] = table_row[i];
+    for (int32_t i = max_blocks_per_seq - n; i < max_blocks_per_seq; ++i) table_row[i] = -1;
+    *table_offset += n;
+    return PKV_OK;
+}
+
 }  // extern "C"

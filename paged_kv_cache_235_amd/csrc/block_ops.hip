@@ -17,10 +17,13 @@
 namespace pkv {
 
 __global__ __launch_bounds__(256) void slot_mapping_kernel(const int32_t* cu_q_lens, const int32_t* seq_lens,
-                                                           const int32_t* block_tables, int32_t max_blocks,
+                                                           const int32_t* block_tables,
+                                                           const int32_t* table_offsets, int32_t max_blocks,
                                                            int32_t block_size, int32_t num_blocks,
                                                            int32_t* slots, int32_t total_rows) {
     const int s = blockIdx.x;
+    // column c of the row holds logical block c + off
+    const int64_t off = table_offsets ? max(0, table_offsets[s]) : 0;
     const int r0 = cu_q_lens[s];
     const int r1 = cu_q_lens[s + 1];
     const int64_t first = (int64_t)seq_lens[s] - (r1 - r0);   // position of row r0
@@ -28,8 +31,9 @@ __global__ __launch_bounds__(256) void slot_mapping_kernel(const int32_t* cu_q_l
         if (r < 0 || r >= total_rows) continue;
         const int64_t p = first + (r - r0);
         int32_t slot = -1;
-        if (p >= 0 && p / block_size < max_blocks) {
-            const int32_t id = block_tables[(int64_t)s * max_blocks + p / block_size];
+        const int64_t col = p / block_size - off;
+        if (p >= 0 && col >= 0 && col < max_blocks) {
+            const int32_t id = block_tables[(int64_t)s * max_blocks + col];
             if (id >= 0 && id < num_blocks) slot = (int32_t)((int64_t)id * block_size + p % block_size);
         }
         slots[r] = slot;
@@ -82,8 +86,8 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyArgs a) {
 
 hipError_t launch_slot_mapping(const SlotMappingLaunch& L, hipStream_t stream) {
     return launch(slot_mapping_kernel, dim3(L.num_seqs), dim3(256), 0, stream, L.cu_q_lens, L.seq_lens,
-                  L.block_tables, L.max_blocks_per_seq, L.block_size, L.num_blocks, L.slot_mapping,
-                  L.total_rows);
+                  L.block_tables, L.table_offsets, L.max_blocks_per_seq, L.block_size, L.num_blocks,
+                  L.slot_mapping, L.total_rows);
 }
 
 hipError_t launch_copy_blocks(const CopyBlocksLaunch& L, hipStream_t stream) {

@@ -55,6 +55,7 @@ struct DecodeArgs {
     const uint16_t* k_scale;
     const uint16_t* v_scale;
     const int32_t* block_tables;
+    const int32_t* table_offsets;   // per sequence: logical block of column 0 (null: all 0)
     const int32_t* context_lens;
     int32_t num_seqs, num_q_heads, num_kv_heads, group, head_chunks, num_blocks, max_blocks;
     int32_t window, part_tokens, max_parts;
@@ -87,18 +88,28 @@ struct Cfg {
 
 // Number of partitions of sequence s that contain a visible key (1 for an
 // empty context: an item that writes the zero row).
-__device__ __forceinline__ int seq_len(const DecodeArgs& a, int s) {
-    int L = a.context_lens[s];
-    const int cap = a.max_blocks * kBlk;
-    return L < 0 ? 0 : (L > cap ? cap : L);
+__device__ __forceinline__ int seq_off(const DecodeArgs& a, int s) {
+    return a.table_offsets ? max(0, a.table_offsets[s]) : 0;
 }
-__device__ __forceinline__ int first_key(const DecodeArgs& a, int L) {
-    return (a.window > 0 && L > a.window) ? L - a.window : 0;
+// the context length, clamped to what the table row can address
+__device__ __forceinline__ int seq_len(const DecodeArgs& a, int s) {
+    const int L = a.context_lens[s];
+    const int64_t cap = ((int64_t)a.max_blocks + seq_off(a, s)) * kBlk;
+    return L < 0 ? 0 : (L > cap ? (int)cap : L);
+}
+// First visible key: the window's start, and never before the row's first
+// block (keys of released blocks do not exist for the kernels), so the keys of
+// a sequence span at most max_blocks * 16 positions.
+__device__ __forceinline__ int first_key(const DecodeArgs& a, int L, int off) {
+    const int lo = (a.window > 0 && L > a.window) ? L - a.window : 0;
+    return max(lo, off * kBlk);
 }
 __device__ __forceinline__ int num_parts(const DecodeArgs& a, int s) {
     const int L = seq_len(a, s);
     if (L == 0 || a.part_tokens == 0) return 1;
-    return (L - 1) / a.part_tokens - first_key(a, L) / a.part_tokens + 1;
+    const int lo = first_key(a, L, seq_off(a, s));
+    if (lo >= L) return 1;                      // no key left: one item writes the zero row
+    return (L - 1) / a.part_tokens - lo / a.part_tokens + 1;
 }
 
 template <int WORDS>
@@ -234,7 +245,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
 
     // work item -> (sequence, partition, KV head, query-head chunk) and its key range
     struct Item {
-        int s, nparts, k, t0, t1, g, h0, nh;
+        int s, nparts, k, kr, t0, t1, g, h0, nh, off;   // kr: k - the first partition with keys
     };
     auto item_info = [&](int item) {
         Item I;
@@ -253,9 +264,11 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
         const int ps = uni(s_prefix[I.s]);
         I.nparts = uni(s_prefix[I.s + 1]) - ps;
         const int L = uni(s_len[I.s]);
-        const int lo = first_key(a, L);
+        const int lo = min(first_key(a, L, uni(seq_off(a, I.s))), L);
         const int P = a.part_tokens;
         I.k = (P > 0 ? lo / P : 0) + (gp - ps);
+        I.kr = gp - ps;
+        I.off = uni(seq_off(a, I.s));
         I.t0 = P > 0 ? max(lo, I.k * P) : lo;
         I.t1 = P > 0 ? min(L, (I.k + 1) * P) : L;
         I.h0 = I.g * a.group + hchunk * GT;         // first query head of the item
@@ -311,7 +324,10 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
     uint64_t okmask = 0;
     auto ids_of = [&](const Item& I, int c0, int nbw) {
         int id = -1;
-        if (lane < nbw) id = a.block_tables[(int64_t)I.s * a.max_blocks + c0 / kBlk + wave + kWaves * lane];
+        // column of the lane's block in the sequence's row (blocks before the row's
+        // offset have been released: no id)
+        const int col = c0 / kBlk + wave + kWaves * lane - I.off;
+        if (lane < nbw && col >= 0 && col < a.max_blocks) id = a.block_tables[(int64_t)I.s * a.max_blocks + col];
         return id;
     };
     auto valid_id = [&](int id) { return id >= 0 && id < a.num_blocks; };
@@ -376,7 +392,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
         if (dyn && wave == 0 && lane == 0 && following < total) claimed = (int)atomicAdd(a.ticket, 1u);
         const bool have_next = following < total;
         const Item NI = item_info(have_next ? following : item);
-        const int s = I.s, g = I.g, h0 = I.h0, nh = I.nh, k = I.k, nparts = I.nparts;
+        const int s = I.s, g = I.g, h0 = I.h0, nh = I.nh, k = I.kr, nparts = I.nparts;
 
         // running softmax state of this wave's keys: m per head (uniform), the
         // same m per logit slot of this lane, l per logit slot, acc per column
@@ -676,10 +692,9 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecodeArgs a) {
     const int s = pair / a.num_q_heads;
     const int n = num_parts(a, s);
     if (n <= 1) return;
-    const int L = seq_len(a, s);
-    const int k0 = first_key(a, L) / a.part_tokens;
-    const float* ml = a.part_ml + ((int64_t)pair * a.max_parts + k0) * 2;
-    const float* po = a.part_o + ((int64_t)pair * a.max_parts + k0) * D + lane * E;
+    // partials are stored from the sequence's first partition with visible keys
+    const float* ml = a.part_ml + (int64_t)pair * a.max_parts * 2;
+    const float* po = a.part_o + (int64_t)pair * a.max_parts * D + lane * E;
 
     float M = -INFINITY;
     for (int k = lane; k < n; k += kWave) M = fmaxf(M, ml[2 * k]);
@@ -757,10 +772,13 @@ static PartKernel pick(KvKind kv, int D, int gt) {
     return D == 64 ? pick_gt<KV_I8, 64>(gt) : pick_gt<KV_I8, 128>(gt);
 }
 
-int32_t decode_max_partitions(int32_t max_blocks_per_seq, int32_t block_size, int32_t partition_size) {
+int32_t decode_max_partitions(int32_t max_blocks_per_seq, int32_t block_size, int32_t partition_size,
+                              bool with_table_offsets) {
     if (partition_size <= 0) return 0;
     const int64_t cap = (int64_t)max_blocks_per_seq * block_size;
-    const int64_t n = (cap + partition_size - 1) / partition_size;
+    // with offset rows the keys a row addresses need not start on a partition
+    // boundary, so they can straddle one more partition
+    const int64_t n = (cap + partition_size - 1) / partition_size + (with_table_offsets ? 1 : 0);
     return n <= 1 ? 0 : (int32_t)n;
 }
 
@@ -776,7 +794,8 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
     const int G = L.num_q_heads / L.num_kv_heads;
     const int chunks = (G + kMaxGroup - 1) / kMaxGroup;
     const int gt = (G + chunks - 1) / chunks;
-    const int max_parts = decode_max_partitions(L.max_blocks_per_seq, L.block_size, L.partition_size);
+    const int max_parts = decode_max_partitions(L.max_blocks_per_seq, L.block_size, L.partition_size,
+                                                L.table_offsets != nullptr);
     const bool merge = max_parts > 1;
 
     DecodeArgs a;
@@ -792,6 +811,7 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
     a.head_chunks = chunks;
     a.num_blocks = L.num_blocks;
     a.max_blocks = L.max_blocks_per_seq;
+    a.table_offsets = nullptr;          // set per launch below
     a.window = L.window;
     a.part_tokens = merge ? L.partition_size : 0;
     a.max_parts = merge ? max_parts : 1;
@@ -826,6 +846,7 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
         b.q = static_cast<const char*>(L.q) + qoff * (L.q_bf16 ? 2 : 4);
         b.out = static_cast<char*>(L.out) + qoff * (L.out_bf16 ? 2 : 4);
         b.block_tables = L.block_tables + (int64_t)s0 * L.max_blocks_per_seq;
+        b.table_offsets = L.table_offsets ? L.table_offsets + s0 : nullptr;
         b.context_lens = L.context_lens + s0;
         b.part_ml = merge ? ml_base + (int64_t)s0 * L.num_q_heads * max_parts * 2 : nullptr;
         b.part_o = merge ? o_base + (int64_t)s0 * L.num_q_heads * max_parts * L.head_dim : nullptr;

@@ -82,16 +82,19 @@ int copy_to_host(std::vector<T>& dst, const T* src, size_t n, hipStream_t stream
 // PKV_VALIDATE=1: check device-resident tables and lengths on the host.
 // Entries wholly before the window of the call's first query may be -1 (evicted).
 int validate_tables(const pkv_cache_desc* c, int32_t num_seqs, const int32_t* block_tables,
-                    int32_t max_blocks, const int32_t* lens, const int32_t* cu, int32_t window,
-                    hipStream_t stream) {
-    std::vector<int32_t> L, T, CU;
+                    int32_t max_blocks, const int32_t* offsets, const int32_t* lens, const int32_t* cu,
+                    int32_t window, hipStream_t stream) {
+    std::vector<int32_t> L, T, CU, OFF;
     int rc = copy_to_host(L, lens, (size_t)num_seqs, stream);
     if (rc == PKV_OK) rc = copy_to_host(T, block_tables, (size_t)num_seqs * max_blocks, stream);
     if (rc == PKV_OK && cu) rc = copy_to_host(CU, cu, (size_t)num_seqs + 1, stream);
+    if (rc == PKV_OK && offsets) rc = copy_to_host(OFF, offsets, (size_t)num_seqs, stream);
     if (rc != PKV_OK) return rc;
     if (cu && CU[0] != 0) return fail(PKV_EINVAL, "cu_q_lens[0] = %d, expected 0", CU[0]);
     for (int32_t s = 0; s < num_seqs; ++s) {
-        const int64_t cap = (int64_t)max_blocks * c->block_size;
+        const int64_t off = offsets ? OFF[s] : 0;
+        if (off < 0) return fail(PKV_EINVAL, "table_offsets[%d] = %lld is negative", s, (long long)off);
+        const int64_t cap = ((int64_t)max_blocks + off) * c->block_size;
         if (L[s] < 0 || L[s] > cap)
             return fail(PKV_EINVAL, "length %d of sequence %d outside [0, %lld]", L[s], s, (long long)cap);
         if (cu) {
@@ -101,10 +104,14 @@ int validate_tables(const pkv_cache_desc* c, int32_t num_seqs, const int32_t* bl
         const int32_t used = (L[s] + c->block_size - 1) / c->block_size;
         const int64_t first_query = cu ? (int64_t)L[s] - (CU[s + 1] - CU[s]) : (int64_t)L[s] - 1;
         const int64_t first_key = window > 0 ? std::max<int64_t>(0, first_query - window + 1) : 0;
+        if (first_key / c->block_size < off)
+            return fail(PKV_EINVAL, "sequence %d: keys from %lld are visible but its row starts at block %lld", s,
+                        (long long)first_key, (long long)off);
         for (int32_t b = (int32_t)(first_key / c->block_size); b < used; ++b) {
-            const int32_t id = T[(size_t)s * max_blocks + b];
+            const int32_t id = T[(size_t)s * max_blocks + (b - off)];
             if (id < 0 || id >= c->num_blocks)
-                return fail(PKV_EINVAL, "block_tables[%d][%d] = %d outside [0, %d)", s, b, id, c->num_blocks);
+                return fail(PKV_EINVAL, "block_tables[%d][%lld] = %d outside [0, %d)", s, (long long)(b - off), id,
+                            c->num_blocks);
         }
     }
     return PKV_OK;
@@ -219,11 +226,12 @@ int kv_cache_write(const pkv_cache_desc* cache, const void* k, const void* v, in
 
 size_t paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                              int32_t max_blocks_per_seq, int32_t block_size,
-                                             int32_t partition_size) {
+                                             int32_t partition_size, int32_t with_table_offsets) {
     if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0 || max_blocks_per_seq <= 0 || block_size <= 0 ||
         partition_size < 0)
         return 0;
-    const int32_t np = pkv::decode_max_partitions(max_blocks_per_seq, block_size, partition_size);
+    const int32_t np = pkv::decode_max_partitions(max_blocks_per_seq, block_size, partition_size,
+                                                  with_table_offsets != 0);
     return pkv::decode_workspace_bytes(num_seqs, num_q_heads, head_dim, np);
 }
 
@@ -231,8 +239,9 @@ int paged_attention_decode(const pkv_cache_desc* cache, const void* q, int32_t q
                            int32_t out_dtype, int32_t num_seqs, int32_t num_q_heads, const void* k_pool,
                            const void* v_pool, const void* k_scale, const void* v_scale,
                            const int32_t* block_tables, int32_t max_blocks_per_seq,
-                           const int32_t* context_lens, float softmax_scale, int32_t sliding_window,
-                           int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
+                           const int32_t* table_offsets, const int32_t* context_lens, float softmax_scale,
+                           int32_t sliding_window, int32_t partition_size, void* workspace,
+                           size_t workspace_bytes, void* stream) {
     g_error.clear();
     int rc = check_cache(cache);
     if (rc != PKV_OK) return rc;
@@ -261,14 +270,15 @@ int paged_attention_decode(const pkv_cache_desc* cache, const void* q, int32_t q
     if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16))
         return fail(PKV_EINVAL, "q, out and the pools must be 16-byte aligned");
     const size_t need = paged_attention_decode_workspace_size(num_seqs, num_q_heads, cache->head_dim,
-                                                              max_blocks_per_seq, cache->block_size, partition_size);
+                                                              max_blocks_per_seq, cache->block_size, partition_size,
+                                                              table_offsets != nullptr);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(PKV_EWORKSPACE, "workspace of %zu bytes needed (got %zu)", need, workspace ? workspace_bytes : (size_t)0);
     if (need > 0 && !aligned(workspace, 256)) return fail(PKV_EINVAL, "workspace must be 256-byte aligned");
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (validate_env()) {
-        rc = validate_tables(cache, num_seqs, block_tables, max_blocks_per_seq, context_lens, nullptr,
-                             sliding_window, st);
+        rc = validate_tables(cache, num_seqs, block_tables, max_blocks_per_seq, table_offsets, context_lens,
+                             nullptr, sliding_window, st);
         if (rc != PKV_OK) return rc;
     }
     pkv::DecodeLaunch L;
@@ -290,6 +300,7 @@ int paged_attention_decode(const pkv_cache_desc* cache, const void* q, int32_t q
     L.v_scale = static_cast<const uint16_t*>(v_scale);
     L.block_tables = block_tables;
     L.max_blocks_per_seq = max_blocks_per_seq;
+    L.table_offsets = table_offsets;
     L.context_lens = context_lens;
     L.softmax_scale = softmax_scale;
     L.window = sliding_window;
@@ -306,7 +317,8 @@ int paged_attention_prefill_chunk(const pkv_cache_desc* cache, const void* q, in
                                   int32_t max_q_len, int32_t num_q_heads, const void* k_pool,
                                   const void* v_pool, const void* k_scale, const void* v_scale,
                                   const int32_t* block_tables,
-                                  int32_t max_blocks_per_seq, const int32_t* seq_lens, float softmax_scale,
+                                  int32_t max_blocks_per_seq, const int32_t* table_offsets,
+                                  const int32_t* seq_lens, float softmax_scale,
                                   int32_t sliding_window, void* stream) {
     g_error.clear();
     int rc = check_cache(cache);
@@ -339,8 +351,8 @@ int paged_attention_prefill_chunk(const pkv_cache_desc* cache, const void* q, in
         return fail(PKV_EINVAL, "q, out and the pools must be 16-byte aligned");
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (validate_env()) {
-        rc = validate_tables(cache, num_seqs, block_tables, max_blocks_per_seq, seq_lens, cu_q_lens,
-                             sliding_window, st);
+        rc = validate_tables(cache, num_seqs, block_tables, max_blocks_per_seq, table_offsets, seq_lens,
+                             cu_q_lens, sliding_window, st);
         if (rc != PKV_OK) return rc;
     }
     pkv::PrefillLaunch L;
@@ -362,6 +374,7 @@ int paged_attention_prefill_chunk(const pkv_cache_desc* cache, const void* q, in
     L.v_scale = static_cast<const uint16_t*>(v_scale);
     L.block_tables = block_tables;
     L.max_blocks_per_seq = max_blocks_per_seq;
+    L.table_offsets = table_offsets;
     L.seq_lens = seq_lens;
     L.softmax_scale = softmax_scale;
     L.window = sliding_window;
@@ -372,7 +385,8 @@ int paged_attention_prefill_chunk(const pkv_cache_desc* cache, const void* q, in
 
 int pkv_build_slot_mapping(const pkv_cache_desc* cache, const int32_t* cu_q_lens, int32_t num_seqs,
                            const int32_t* seq_lens, const int32_t* block_tables, int32_t max_blocks_per_seq,
-                           int32_t* slot_mapping, int32_t total_rows, void* stream) {
+                           const int32_t* table_offsets, int32_t* slot_mapping, int32_t total_rows,
+                           void* stream) {
     g_error.clear();
     int rc = check_cache(cache);
     if (rc != PKV_OK) return rc;
@@ -396,6 +410,7 @@ int pkv_build_slot_mapping(const pkv_cache_desc* cache, const int32_t* cu_q_lens
     L.cu_q_lens = cu_q_lens;
     L.seq_lens = seq_lens;
     L.block_tables = block_tables;
+    L.table_offsets = table_offsets;
     L.num_seqs = num_seqs;
     L.max_blocks_per_seq = max_blocks_per_seq;
     L.block_size = cache->block_size;

@@ -57,6 +57,7 @@ struct DecodeLaunch {
     const uint16_t* v_scale;
     const int32_t* block_tables;
     int32_t max_blocks_per_seq;
+    const int32_t* table_offsets;  // per sequence, or null
     const int32_t* context_lens;
     float softmax_scale;
     int32_t window;
@@ -66,7 +67,8 @@ struct DecodeLaunch {
     hipEvent_t start_event;    // recorded right before the partition kernel when non-null
 };
 // Number of partition slots per (sequence, head) in the workspace (0 if no merge).
-int32_t decode_max_partitions(int32_t max_blocks_per_seq, int32_t block_size, int32_t partition_size);
+int32_t decode_max_partitions(int32_t max_blocks_per_seq, int32_t block_size, int32_t partition_size,
+                              bool with_table_offsets);
 size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                               int32_t max_partitions);
 hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream);
@@ -84,6 +86,7 @@ struct PrefillLaunch {
     const uint16_t* v_scale;
     const int32_t* block_tables;
     int32_t max_blocks_per_seq;
+    const int32_t* table_offsets;  // per sequence, or null
     const int32_t* seq_lens;
     float softmax_scale;
     int32_t window;
@@ -94,6 +97,7 @@ struct SlotMappingLaunch {
     const int32_t* cu_q_lens;
     const int32_t* seq_lens;
     const int32_t* block_tables;
+    const int32_t* table_offsets;  // per sequence, or null
     int32_t num_seqs, max_blocks_per_seq, block_size, num_blocks;
     int32_t* slot_mapping;
     int32_t total_rows;

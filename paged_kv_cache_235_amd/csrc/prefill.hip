@@ -71,6 +71,7 @@ struct PrefillArgs {
     const uint16_t* k_scale;    // INT8 pools: fp16 scales [blocks][heads][16]
     const uint16_t* v_scale;
     const int32_t* block_tables;
+    const int32_t* table_offsets;   // per sequence: logical block of column 0 (null: all 0)
     const int32_t* seq_lens;
     const int32_t* cu_q_lens;
     int32_t num_seqs, num_q_heads, num_kv_heads, group, num_blocks, max_blocks;
@@ -123,7 +124,9 @@ __global__ __launch_bounds__(64 * W) void prefill_pipe_kernel(PrefillArgs a) {
     const int G = a.group;
     const int q0 = a.cu_q_lens[s];
     const int C = a.cu_q_lens[s + 1] - q0;
-    const int L = min(a.seq_lens[s], a.max_blocks * kBlk);
+    // column c of the sequence's row holds logical block c + off (blocks before it released)
+    const int off = a.table_offsets ? max(0, a.table_offsets[s]) : 0;
+    const int L = (int)min((int64_t)a.seq_lens[s], ((int64_t)a.max_blocks + off) * kBlk);
     const int nrows = C * G;
     const int r0 = mt * ROWS;
     if (r0 >= nrows || C <= 0 || C > L) return;
@@ -162,13 +165,15 @@ __global__ __launch_bounds__(64 * W) void prefill_pipe_kernel(PrefillArgs a) {
     float l_run = 0.0f;          // this lane's share of the row sum
 
     const int k_lo = (a.window > 0) ? max(0, p_min - a.window + 1) : 0;
-    const int kt_first = (k_lo / kKeys) * kKeys;
+    // tiles of 64 keys from a 64-key boundary, but never before the row's first
+    // block (tiles need only block alignment), so every table read is in the row
+    const int kt_first = max((k_lo / kKeys) * kKeys, off * kBlk);
     const int n_tiles = kt_first <= p_max ? (p_max - kt_first) / kKeys + 1 : 0;
     const int last_blk = (L - 1) / kBlk;        // last logical block with keys
     // read-only during the kernel: through the constant address space its reads stay
     // scalar loads whatever else the kernel does
     const __attribute__((address_space(4))) int32_t* table =
-        (const __attribute__((address_space(4))) int32_t*)(a.block_tables + (int64_t)s * a.max_blocks);
+        (const __attribute__((address_space(4))) int32_t*)(a.block_tables + (int64_t)s * a.max_blocks - off);
     const int64_t head_stride = (int64_t)kBlk * D;          // elements per (block, head) tile
     const int64_t blk_stride = (int64_t)a.num_kv_heads * head_stride;
 
@@ -193,7 +198,7 @@ __global__ __launch_bounds__(64 * W) void prefill_pipe_kernel(PrefillArgs a) {
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const int lb = kt / kBlk + b;
-            const int id = lb <= last_blk ? table[lb] : -1;
+            const int id = lb <= last_blk ? table[lb] : -1;   // lb >= off: kt_first
             const bool ok = id >= 0 && id < a.num_blocks;
             got[b] = ok ? id : 0;               // an invalid block reads block 0 and is masked
             m |= (ok ? 1 : 0) << b;
@@ -559,6 +564,7 @@ hipError_t launch_prefill(const PrefillLaunch& L, hipStream_t stream) {
     a.k_scale = L.k_scale;
     a.v_scale = L.v_scale;
     a.block_tables = L.block_tables;
+    a.table_offsets = L.table_offsets;
     a.seq_lens = L.seq_lens;
     a.cu_q_lens = L.cu_q_lens;
     a.num_seqs = L.num_seqs;

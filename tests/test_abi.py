@@ -53,11 +53,11 @@ FAKE = ctypes.c_void_p(0x1000)          # never dereferenced: every call below f
 
 def _decode(lib, desc, **kw):
     a = dict(q=FAKE, q_dtype=BF16, out=FAKE, out_dtype=F32, num_seqs=2, hq=4, k=FAKE, v=FAKE, ks=None, vs=None,
-             tables=FAKE, maxb=4, lens=FAKE, scale=0.1, window=0, part=0, ws=None, wsb=0)
+             tables=FAKE, maxb=4, offs=None, lens=FAKE, scale=0.1, window=0, part=0, ws=None, wsb=0)
     a.update(kw)
     return lib.paged_attention_decode(ctypes.byref(desc), a["q"], a["q_dtype"], a["out"], a["out_dtype"],
                                       a["num_seqs"], a["hq"], a["k"], a["v"], a["ks"], a["vs"], a["tables"],
-                                      a["maxb"], a["lens"], a["scale"], a["window"], a["part"], a["ws"],
+                                      a["maxb"], a["offs"], a["lens"], a["scale"], a["window"], a["part"], a["ws"],
                                       a["wsb"], None)
 
 
@@ -81,16 +81,20 @@ def test_decode_validation(lib):
     assert _decode(lib, _desc(), maxb=4, part=16) == PKV_EWORKSPACE      # 4 partitions need scratch
     assert b"workspace" in lib.pkv_last_error()
     assert _decode(lib, _desc(), maxb=4, part=16, ws=ctypes.c_void_p(0x1010), wsb=1 << 20) == PKV_EINVAL  # misaligned
+    # offset rows: one row-wide partition may straddle two, so scratch is needed
+    assert _decode(lib, _desc(), maxb=4, part=64, offs=FAKE) == PKV_EWORKSPACE
 
 
 def test_workspace_size(lib):
     f = lib.paged_attention_decode_workspace_size
-    assert f(8, 32, 128, 256, 16, 0) == 0                   # single pass
-    assert f(8, 32, 128, 32, 16, 512) == 0                  # one partition covers everything
-    n = f(256, 32, 128, 2048, 16, 512)
+    assert f(8, 32, 128, 256, 16, 0, 0) == 0                # single pass
+    assert f(8, 32, 128, 32, 16, 512, 0) == 0               # one partition covers everything
+    assert f(8, 32, 128, 32, 16, 512, 1) > 0                # ... unless offset rows straddle two
+    n = f(256, 32, 128, 2048, 16, 512, 0)
     slots = 256 * 32 * 64
     assert n >= slots * (128 + 2) * 4 and n < slots * (128 + 2) * 4 + 512
-    assert f(-1, 32, 128, 2048, 16, 512) == 0
+    assert f(256, 32, 128, 2048, 16, 512, 1) > n            # one more partition per (sequence, head)
+    assert f(-1, 32, 128, 2048, 16, 512, 0) == 0
 
 
 def test_write_validation(lib):
@@ -112,7 +116,7 @@ def test_prefill_validation(lib):
     d = _desc()
     args = lambda **k: (ctypes.byref(k.get("desc", d)), FAKE, k.get("qd", BF16), FAKE, F32, FAKE,
                         k.get("b", 2), k.get("mq", 16), k.get("hq", 8), FAKE, FAKE, k.get("ks"), k.get("vs"),
-                        FAKE, 4, FAKE, 0.1, k.get("w", 0), None)
+                        FAKE, 4, None, FAKE, 0.1, k.get("w", 0), None)
     assert p(*args(b=0)) == PKV_OK
     assert p(*args(mq=0)) == PKV_OK
     assert p(*args(qd=F32)) == PKV_EUNSUPPORTED
@@ -134,7 +138,7 @@ def test_slot_mapping_validation(lib):
     f = lib.pkv_build_slot_mapping
     d = _desc()
     args = lambda **k: (ctypes.byref(k.get("desc", d)), k.get("cu", FAKE), k.get("b", 2), k.get("lens", FAKE),
-                        k.get("tables", FAKE), k.get("maxb", 4), k.get("out", FAKE), k.get("rows", 10), None)
+                        k.get("tables", FAKE), k.get("maxb", 4), None, k.get("out", FAKE), k.get("rows", 10), None)
     assert f(*args(b=0)) == PKV_OK                       # nothing to do: no launch
     assert f(*args(rows=0)) == PKV_OK
     assert f(*args(b=-1)) == PKV_EINVAL
@@ -143,7 +147,7 @@ def test_slot_mapping_validation(lib):
     assert f(*args(cu=None)) == PKV_EINVAL
     assert f(*args(out=None)) == PKV_EINVAL
     assert f(*args(desc=_desc(bs=32))) == PKV_EUNSUPPORTED
-    assert f(None, FAKE, 2, FAKE, FAKE, 4, FAKE, 10, None) == PKV_EINVAL
+    assert f(None, FAKE, 2, FAKE, FAKE, 4, None, FAKE, 10, None) == PKV_EINVAL
     assert lib.pkv_last_error()                          # the reason is reported
 
 

@@ -153,3 +153,20 @@ def test_evict_window_releases_exactly_the_dead_blocks(length, window):
     assert n == sum(1 for b in range(_blocks(length)) if row[b] == -1)
     assert a.num_free == 400 - _blocks(length) + n
     assert a.evict_window(row, length, window) == 0  # idempotent
+
+
+def test_compact_moves_released_entries_into_the_offset():
+    a = pkv.BlockAllocator(64)
+    row = np.full(10, -1, np.int32)
+    a.append(row, 0, 150)                           # 10 blocks
+    held = row.copy()
+    assert a.evict_window(row, 150, 40) == 6        # keys <= 110 are gone: blocks 0..5 (block 6 holds 111)
+    off = pkv.BlockAllocator.compact(row, 0)
+    assert off == 6 and np.array_equal(row[:4], held[6:10]) and (row[4:] == -1).all()
+    # the compacted row works as a plain row of the positions from off * 16 on
+    assert a.append(row, 150 - off * 16, 40) == []  # 190 tokens: logical blocks 10, 11 -> columns 4, 5
+    assert (row[4:6] >= 0).all() and (row[6:] == -1).all()
+    assert a.evict_window(row, 190 - off * 16, 40) == 3   # keys <= 150 gone: logical 6, 7, 8 -> columns 0..2
+    off = pkv.BlockAllocator.compact(row, off)
+    assert off == 9 and (row[:3] >= 0).all() and (row[3:] == -1).all()
+    assert pkv.BlockAllocator.compact(np.full(4, -1, np.int32), 3) == 3   # nothing held: unchanged

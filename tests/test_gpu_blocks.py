@@ -294,3 +294,109 @@ def test_window_eviction_changes_no_output_bit(window):
     assert torch.equal(dec1, dec0)
     assert torch.equal(pre1, pre0)
     assert np.array_equal(dref1, dref) and np.array_equal(pref1, pref)   # the oracle agrees
+
+
+# ------------------------------------------------------------ offset rows
+def _compact_rows(case, W):
+    """Rows that keep only the blocks from each sequence's first visible one
+    ("MicroGen", Key Features: window eviction), and their offsets."""
+    offs, rows = [], []
+    for s in range(case.num_seqs):
+        first_query = int(case.seq_lens[s]) - int(case.new_lens[s])
+        offs.append(max(0, first_query - W + 1) // BS)
+        rows.append(case.block_tables[s, offs[-1]:-(-int(case.seq_lens[s]) // BS)])
+    width = max(len(r) for r in rows)
+    out = np.full((case.num_seqs, width), -1, np.int32)
+    for s, r in enumerate(rows):
+        out[s, :len(r)] = r
+    return out, np.array(offs, np.int32)
+
+
+@pytest.mark.parametrize("kind,part", [("decode", 64), ("decode", 0), ("decode", 512), ("prefill", 0)])
+def test_offset_rows_equal_full_tables(kind, part):
+    from pkv_testlib import alloc_pools, run_decode, run_prefill, tables, write_tokens
+    from oracle.cases import expected_outputs
+    W = 200
+    lens = [1500, 700, 260, 4000, 64]
+    new = [1] * 5 if kind == "decode" else [30, 1, 64, 100, 5]
+    case = workloads.make_case("offsets", 77, lens, new, 8, 2, 128, window=W, kind=kind, partition_size=max(part, 16))
+    dev = device()
+    pools = alloc_pools(case, dev)
+    write_tokens(case, pools, dev, "all")
+    full = run_decode(case, pools, dev, partition_size=part) if kind == "decode" else run_prefill(case, pools, dev)
+    rows, offs = _compact_rows(case, W)
+    assert offs.max() > 0 and rows.shape[1] < case.block_tables.shape[1]
+    bt, lens_t, cu = tables(case, dev)
+    rows_t = torch.from_numpy(rows).to(dev)
+    offs_t = torch.from_numpy(offs).to(dev)
+    q = case.q(dev)
+    if kind == "decode":
+        got = pkv.paged_attention_decode(q, pools["k"], pools["v"], rows_t, lens_t, case.softmax_scale,
+                                         sliding_window=W, partition_size=part, table_offsets=offs_t)
+    else:
+        got = pkv.paged_attention_prefill_chunk(q, cu, lens_t, pools["k"], pools["v"], rows_t, case.max_q_len,
+                                                case.softmax_scale, sliding_window=W, table_offsets=offs_t)
+    torch.cuda.synchronize()
+    if kind == "decode" and part in (0, 512):
+        assert torch.equal(got, full)        # the same blocks, the same work split
+    # (prefill starts its first key tile at the row's first block, which may move
+    # a tile boundary: equal to the oracle, not necessarily bit for bit)
+    assert_close(got, expected_outputs(case), "bf16", f"{kind} offsets P={part}")
+    slots = pkv.build_slot_mapping(cu, lens_t, rows_t, pools["k"], table_offsets=offs_t)
+    ref = oracle.slot_mapping(case.num_blocks, BS, case.cu_q_lens, case.seq_lens, rows, table_offsets=offs)
+    assert np.array_equal(slots.cpu().numpy(), ref) and np.array_equal(ref, case.new_slots())
+
+
+def test_offset_rows_without_a_window_see_only_the_rows_keys():
+    """Keys of blocks before a row's offset do not exist for the kernels; with no
+    window the result is attention over the row's keys, the same as a window
+    that starts at the row (and every access stays inside the row)."""
+    from pkv_testlib import alloc_pools, write_tokens
+    case = workloads.make_case("offsets-nowin", 78, [900], [1], 8, 2, 128)
+    dev = device()
+    pools = alloc_pools(case, dev)
+    write_tokens(case, pools, dev, "all")
+    off = 20
+    rows = torch.from_numpy(np.ascontiguousarray(case.block_tables[:, off:])).to(dev)
+    offs = torch.tensor([off], dtype=torch.int32, device=dev)
+    lens = torch.from_numpy(case.seq_lens).to(dev)
+    q = case.q(dev)
+    outs = []
+    for W in (0, 900 - off * BS):
+        for part in (64, 0):
+            outs.append(pkv.paged_attention_decode(q, pools["k"], pools["v"], rows, lens, case.softmax_scale,
+                                                   sliding_window=W, partition_size=part, table_offsets=offs))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[2]) and torch.equal(outs[1], outs[3])
+    from oracle.cases import expected_outputs
+    import dataclasses
+    windowed = dataclasses.replace(case, window=900 - off * BS)
+    assert_close(outs[0], expected_outputs(windowed), "bf16", "offset row, no window")
+
+
+def test_eviction_then_compaction_keeps_every_output_bit():
+    m = Mirror(num_blocks=200, num_seqs=3, max_blocks=200, hq=8, hkv=2)
+    W, chunk = 64, 16
+    m.append(0, 900)
+    m.append(1, 333)
+    q, qp = m.queries(2), m.queries(2 * chunk)
+    dec0, _ = m.decode([0, 1], q, window=W)
+    pre0, pref = m.prefill([0, 1], chunk, qp, window=W)     # the oracle on the full tables
+    offs = np.zeros(2, np.int32)
+    for s in (0, 1):
+        m.alloc.evict_window(m.rows[s], int(m.lens[s]) - chunk, W)
+        offs[s] = pkv.BlockAllocator.compact(m.rows[s], 0)
+    assert offs.min() > 0
+    width = max(-(-int(m.lens[s]) // BS) - offs[s] for s in (0, 1))
+    rows = torch.from_numpy(np.ascontiguousarray(m.rows[:2, :width])).to(m.dev)
+    offs_t = torch.from_numpy(offs).to(m.dev)
+    lens = m._t(m.lens[:2])
+    dec1 = pkv.paged_attention_decode(q.to(m.dev), m.k, m.v, rows, lens, m.scale, sliding_window=W,
+                                      partition_size=512, table_offsets=offs_t)
+    cu = m._t(np.arange(3, dtype=np.int32) * chunk)
+    pre1 = pkv.paged_attention_prefill_chunk(qp.to(m.dev), cu, lens, m.k, m.v, rows, chunk, m.scale,
+                                             sliding_window=W, table_offsets=offs_t)
+    torch.cuda.synchronize()
+    assert torch.equal(dec1, dec0)
+    assert_close(pre1, pref, "bf16", "prefill over compacted rows")
+    assert_close(pre0, pref, "bf16", "prefill over full rows")
