@@ -312,14 +312,16 @@ def _compact_rows(case, W):
     return out, np.array(offs, np.int32)
 
 
-@pytest.mark.parametrize("kind,part", [("decode", 64), ("decode", 0), ("decode", 512), ("prefill", 0)])
-def test_offset_rows_equal_full_tables(kind, part):
+@pytest.mark.parametrize("kind,part,kv", [("decode", 64, "bf16"), ("decode", 0, "bf16"), ("decode", 512, "bf16"),
+                                          ("prefill", 0, "bf16"), ("decode", 64, "i8"), ("prefill", 0, "i8")])
+def test_offset_rows_equal_full_tables(kind, part, kv):
     from pkv_testlib import alloc_pools, run_decode, run_prefill, tables, write_tokens
     from oracle.cases import expected_outputs
     W = 200
     lens = [1500, 700, 260, 4000, 64]
     new = [1] * 5 if kind == "decode" else [30, 1, 64, 100, 5]
-    case = workloads.make_case("offsets", 77, lens, new, 8, 2, 128, window=W, kind=kind, partition_size=max(part, 16))
+    case = workloads.make_case("offsets", 77, lens, new, 8, 2, 128, window=W, kind=kind, partition_size=max(part, 16),
+                               kv_dtype=kv, outliers=0.01 if kv == "i8" else 0.0)
     dev = device()
     pools = alloc_pools(case, dev)
     write_tokens(case, pools, dev, "all")
@@ -332,10 +334,12 @@ def test_offset_rows_equal_full_tables(kind, part):
     q = case.q(dev)
     if kind == "decode":
         got = pkv.paged_attention_decode(q, pools["k"], pools["v"], rows_t, lens_t, case.softmax_scale,
-                                         sliding_window=W, partition_size=part, table_offsets=offs_t)
+                                         sliding_window=W, partition_size=part, table_offsets=offs_t,
+                                         k_scale=pools["ks"], v_scale=pools["vs"])
     else:
         got = pkv.paged_attention_prefill_chunk(q, cu, lens_t, pools["k"], pools["v"], rows_t, case.max_q_len,
-                                                case.softmax_scale, sliding_window=W, table_offsets=offs_t)
+                                                case.softmax_scale, sliding_window=W, table_offsets=offs_t,
+                                                k_scale=pools["ks"], v_scale=pools["vs"])
     torch.cuda.synchronize()
     if kind == "decode" and part in (0, 512):
         assert torch.equal(got, full)        # the same blocks, the same work split
