@@ -359,7 +359,10 @@ class BlockAllocator:
             self._h = None
 
     def __del__(self):
-        self.close()
+        try:
+            self.close()
+        except Exception:       # interpreter shutdown: the library may already be gone
+            pass
 
     @property
     def num_free(self) -> int:
