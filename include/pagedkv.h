@@ -26,7 +26,8 @@
  *     and pkv_last_error() describes the problem.  No exception crosses the ABI.
  *   - Device-resident integers (slots, block ids, lengths) are read by the
  *     kernels: out-of-range slots and block ids are skipped rather than
- *     dereferenced, lengths are clamped to max_blocks_per_seq * block_size.
+ *     dereferenced, lengths are clamped to what a table row addresses,
+ *     (max_blocks_per_seq + its table offset) * block_size.
  *     Setting the environment variable PKV_VALIDATE=1 makes every call copy
  *     them to the host first (synchronising) and reject bad values with
  *     PKV_EINVAL.
