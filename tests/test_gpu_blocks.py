@@ -137,6 +137,7 @@ class Mirror:
         self.orc = oracle.Cache(num_blocks, BS, hkv, d, "bf16")
         self.rows = np.full((num_seqs, max_blocks), -1, np.int32)
         self.lens = np.zeros(num_seqs, np.int32)
+        self.offs = np.zeros(num_seqs, np.int32)     # first logical block of each row
         self.counter = 0
         self.scale = float(np.float32(1.0 / np.sqrt(d)))
 
@@ -154,8 +155,10 @@ class Mirror:
         L = int(self.lens[s])
         cu = np.array([0, n], np.int32)
         lens = np.array([L + n], np.int32)
-        slots = pkv.build_slot_mapping(self._t(cu), self._t(lens), self._t(row[None, :]), self.k)
-        ref_slots = oracle.slot_mapping(self.nb, BS, cu, lens, row[None, :])
+        off = self.offs[s:s + 1]
+        slots = pkv.build_slot_mapping(self._t(cu), self._t(lens), self._t(row[None, :]), self.k,
+                                       table_offsets=self._t(off))
+        ref_slots = oracle.slot_mapping(self.nb, BS, cu, lens, row[None, :], table_offsets=off)
         assert np.array_equal(slots.cpu().numpy(), ref_slots)
         k = self._values(workloads.TAG_K, n * self.hkv * self.d, n, self.hkv, self.d)
         v = self._values(workloads.TAG_V, n * self.hkv * self.d, n, self.hkv, self.d)
@@ -172,12 +175,14 @@ class Mirror:
         oracle.copy_blocks(self.orc, src, dst)
 
     def append(self, s, n):
-        self.copy(self.alloc.append(self.rows[s], int(self.lens[s]), n))
+        # an offset row addresses positions from offs * 16 on
+        self.copy(self.alloc.append(self.rows[s], int(self.lens[s]) - int(self.offs[s]) * BS, n))
         self.write(s, n)
 
     def fork(self, parent, child):
-        self.alloc.fork(self.rows[parent], int(self.lens[parent]), self.rows[child])
+        self.alloc.fork(self.rows[parent], int(self.lens[parent]) - int(self.offs[parent]) * BS, self.rows[child])
         self.lens[child] = self.lens[parent]
+        self.offs[child] = self.offs[parent]
 
     def queries(self, rows):
         return self._values(workloads.TAG_Q, rows * self.hq * self.d, rows, self.hq, self.d)
@@ -404,3 +409,81 @@ def test_eviction_then_compaction_keeps_every_output_bit():
     assert torch.equal(dec1, dec0)
     assert_close(pre1, pref, "bf16", "prefill over compacted rows")
     assert_close(pre0, pref, "bf16", "prefill over full rows")
+
+
+def test_random_serving_loop_of_table_edits():
+    """Random steps over five sequences -- appends (decode tokens and chunks),
+    forks that share a prefix, rollbacks of draft tokens, window eviction with
+    row compaction -- each mirrored on the oracle's cache; after every few steps
+    decode and prefill over the live rows (with their offsets) match the oracle
+    ("MicroGen", Key Features: paged blocks, prefix sharing, rollback, window
+    eviction)."""
+    rng = np.random.default_rng(2024)
+    W, chunk = 96, 4
+    m = Mirror(num_blocks=400, num_seqs=5, max_blocks=64, hq=8, hkv=2, d=64, seed=91)
+    floor = np.zeros(5, np.int64)   # no rollback below this: keys before it may be evicted
+
+    def evict(s):
+        # evict as of 8 tokens back, so the chunk of rows checked below and
+        # rollbacks down to `floor` still see every key of their windows
+        e = int(m.lens[s]) - 8
+        if e - int(m.offs[s]) * BS <= 0:
+            return
+        m.alloc.evict_window(m.rows[s], e - int(m.offs[s]) * BS, W)
+        m.offs[s] = pkv.BlockAllocator.compact(m.rows[s], int(m.offs[s]))
+        floor[s] = max(floor[s], e + chunk)
+
+    def grow(s, n):
+        if int(m.lens[s]) + n - int(m.offs[s]) * BS > (64 - 2) * BS:
+            evict(s)
+        m.append(s, n)
+
+    for s in range(2):
+        m.append(s, int(rng.integers(20, 200)))
+    live = [0, 1]
+    for step in range(24):
+        op = rng.integers(4)
+        s = int(rng.choice(live))
+        if op == 0 or (op == 1 and len(live) == 5):
+            grow(s, int(rng.choice([1, 1, 1, 7, 33])))
+        elif op == 1:
+            child = [c for c in range(5) if c not in live][0]
+            m.fork(s, child)
+            floor[child] = floor[s]
+            live.append(child)
+            grow(child, int(rng.integers(1, 20)))        # diverges (copy on write of a shared partial block)
+        elif op == 2:
+            L = int(m.lens[s])
+            new = max(int(floor[s]), int(m.offs[s]) * BS + 1, L - int(rng.integers(1, 6)))
+            if new < L:
+                m.alloc.truncate(m.rows[s], L - int(m.offs[s]) * BS, new - int(m.offs[s]) * BS)
+                m.lens[s] = new
+        else:
+            evict(s)
+        if step % 6 == 5:
+            seqs = sorted(live)
+            offs = m._t(m.offs[seqs])
+            q = m.queries(len(seqs))
+            out = pkv.paged_attention_decode(q.to(m.dev), m.k, m.v, m._t(m.rows[seqs]), m._t(m.lens[seqs]), m.scale,
+                                             sliding_window=W, partition_size=64, table_offsets=offs)
+            qp = m.queries(chunk * len(seqs))
+            cu = np.arange(len(seqs) + 1, dtype=np.int32) * chunk
+            outp = pkv.paged_attention_prefill_chunk(qp.to(m.dev), m._t(cu), m._t(m.lens[seqs]), m.k, m.v,
+                                                     m._t(m.rows[seqs]), chunk, m.scale, sliding_window=W,
+                                                     table_offsets=offs)
+            torch.cuda.synchronize()
+            ref = oracle.decode(m.orc, to_numpy(q), "bf16", m.lens[seqs], m.rows[seqs], m.scale, W,
+                                table_offsets=m.offs[seqs])
+            refp = oracle.attention(m.orc, to_numpy(qp), "bf16", cu, m.lens[seqs], m.rows[seqs], m.scale, W,
+                                    table_offsets=m.offs[seqs])
+            assert_close(out, ref, "bf16", f"decode after step {step}")
+            assert_close(outp, refp, "bf16", f"prefill after step {step}")
+    assert (m.offs[live] > 0).any()               # some rows were compacted
+    # every block is held exactly as often as the live rows name it
+    held = {}
+    for s in live:
+        for b in m.rows[s]:
+            if b >= 0:
+                held[int(b)] = held.get(int(b), 0) + 1
+    for b in range(m.nb):
+        assert m.alloc.refcount(b) == held.get(b, 0)
