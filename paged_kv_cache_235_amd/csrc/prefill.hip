@@ -36,7 +36,8 @@
 //  * Online softmax in fp32 with exp2 (scale * log2 e folded in) and a lazy
 //    rescale (the output is rescaled only when a row maximum grows by > 2^8).
 //  * Workgroups of one (sequence, KV head) are placed on the same XCD so the
-//    K/V tiles they all read stay in that XCD's L2.
+//    K/V tiles they all read stay in that XCD's L2; the (sequence, KV head)
+//    units are dealt to the XCDs round-robin, so each gets the same mix.
 //
 // INT8 pools ("MicroGen", Key Features: dynamic per-vector INT8 KV): K codes
 // are staged as bf16 (integers up to 127 are exact), so Q.K^T of the codes is
@@ -114,11 +115,17 @@ __global__ __launch_bounds__(64 * W) void prefill_pipe_kernel(PrefillArgs a) {
     __shared__ __attribute__((aligned(16))) float s_ksc[I8 ? 2 : 1][I8 ? kKeys : 4];  // K scale * scale_log2
     __shared__ __attribute__((aligned(16))) float s_vsc[I8 ? 2 : 1][I8 ? kKeys : 4];  // V scale
 
-    // ---- work item: XCD-major so that one (sequence, head) stays on one XCD
-    const int per_xcd = (a.total + kXcds - 1) / kXcds;
-    const int w_idx = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-    if (w_idx >= a.total) return;
-    const int mt = w_idx % a.m_tiles;
+    // ---- work item: workgroup i runs on XCD i % 8.  (sequence, KV head) units are
+    // dealt round-robin to the XCDs: the row tiles of a unit stay on one XCD and
+    // share its K/V tiles through that XCD's L2, and every XCD gets the same mix
+    // of short and long sequences
+    const int units = a.total / a.m_tiles;
+    const int xcd = blockIdx.x % kXcds;
+    const int j = blockIdx.x / kXcds;                       // position on that XCD
+    const int unit = (j / a.m_tiles) * kXcds + xcd;
+    if (unit >= units) return;
+    const int mt = j % a.m_tiles;
+    const int w_idx = unit * a.m_tiles + mt;
     const int g = (w_idx / a.m_tiles) % a.num_kv_heads;
     const int s = w_idx / (a.m_tiles * a.num_kv_heads);
     const int G = a.group;
@@ -583,7 +590,8 @@ hipError_t launch_prefill(const PrefillLaunch& L, hipStream_t stream) {
     a.window = L.window;
     a.scale_log2 = L.softmax_scale * kLog2e;
     a.out_bf16 = L.out_bf16;
-    const int64_t grid = ((total + kXcds - 1) / kXcds) * kXcds;
+    const int64_t units = (int64_t)L.num_seqs * L.num_kv_heads;
+    const int64_t grid = ((units + kXcds - 1) / kXcds) * a.m_tiles * kXcds;
     const dim3 g3((unsigned)grid), b3(64 * kPipeWaves);
     const bool zs = !(a.scale_log2 > 0.0f);
     if (L.int8) {
