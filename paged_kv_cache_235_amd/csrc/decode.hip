@@ -215,16 +215,20 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
             cnt[i] = (i < per && s < B) ? num_parts(a, s) : 0;
             sum += cnt[i];
         }
-        int* scan = reinterpret_cast<int*>(&s_comb[0][0][0]);
-        scan[tid] = sum;
-        __syncthreads();
-        for (int off = 1; off < kThreads; off <<= 1) {
-            const int add = tid >= off ? scan[tid - off] : 0;
-            __syncthreads();
-            scan[tid] += add;
-            __syncthreads();
+        // inclusive prefix of the per-thread sums: inside each wave by shuffles,
+        // then the waves' totals through LDS (one barrier)
+        int incl = sum;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int up = __shfl_up(incl, off, kWave);
+            if (lane >= off) incl += up;
         }
-        int run = scan[tid] - sum;   // exclusive prefix
+        int* wtot = reinterpret_cast<int*>(&s_comb[0][0][0]);
+        if (lane == kWave - 1) wtot[wave] = incl;
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) incl += w < wave ? wtot[w] : 0;
+        int run = incl - sum;        // exclusive prefix
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int s = tid * per + i;
@@ -234,7 +238,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
             }
             run += cnt[i];
         }
-        if (tid == kThreads - 1) s_prefix[B] = scan[tid];
+        if (tid == kThreads - 1) s_prefix[B] = incl;
         __syncthreads();
     }
 
