@@ -591,6 +591,77 @@ def calibrate_copy(torch):
     print(f"[bench] calibration copy: 3 launches, each {n * 4} bytes read and {n * 4} written", flush=True)
 
 
+def measured_peaks(torch):
+    """What this GPU reaches, beside the published peaks the roofline fractions
+    are quoted against.  The measurement kernels of include/pkv_probe.h: a
+    streaming read of 4 GiB (far past the 256 MiB last-level cache; every
+    16-byte chunk read once, four loads in flight per thread) and bf16 MFMA
+    chains with no memory traffic; best over a few grid sizes.  torch's copy
+    and GEMM are given as library reference points.  Each rate is the mean over
+    back-to-back launches between two events, after untimed launches."""
+    import ctypes
+    from paged_kv_cache_235_amd import _build
+    plib = ctypes.CDLL(_build.PROBE_LIB_PATH)
+    plib.pkv_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32,
+                                           ctypes.c_void_p]
+    plib.pkv_probe_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_uint32,
+                                         ctypes.c_void_p]
+    dev = torch.device("cuda", 0)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def seconds(fn, reps):
+        for _ in range(2):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps / 1e3
+
+    def call(rc):
+        if rc != 0:
+            raise RuntimeError(f"probe launch failed ({rc})")
+
+    nbytes = 4 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    threads = 256
+    read = {}
+    for grid in (2048, 4096, 8192, 16384, 32768):
+        sink = torch.empty(grid * threads, dtype=torch.int32, device=dev)
+        t = seconds(lambda: call(plib.pkv_probe_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes,
+                                                            ctypes.c_void_p(sink.data_ptr()), grid, stream)), 10)
+        read[grid] = nbytes / t / 1e9
+    out = torch.empty_like(buf)
+    t_copy = seconds(lambda: out.copy_(buf), 10)
+    del buf, out
+    mfma = {}
+    iters = 10000
+    for grid in (512, 1024):
+        sink = torch.empty(grid * threads, dtype=torch.float32, device=dev)
+        t = seconds(lambda: call(plib.pkv_probe_mfma_bf16(ctypes.c_void_p(sink.data_ptr()), iters, grid, 1,
+                                                          stream)), 5)
+        mfma[grid] = grid * 4 * iters * 4 * 32768 / t / 1e12
+    m = 8192
+    g = torch.Generator(device=dev).manual_seed(0)
+    a_ = torch.randn(m, m, device=dev, dtype=torch.bfloat16, generator=g)
+    b_ = torch.randn(m, m, device=dev, dtype=torch.bfloat16, generator=g)
+    c_ = torch.empty(m, m, device=dev, dtype=torch.bfloat16)
+    t_mm = seconds(lambda: torch.matmul(a_, b_, out=c_), 20)
+    del a_, b_, c_
+    torch.cuda.empty_cache()
+    return {"hbm_read_GBps": round(max(read.values()), 1),
+            "hbm_read_GBps_by_grid": {str(k): round(v, 1) for k, v in read.items()},
+            "bf16_mfma_TFLOPs": round(max(mfma.values()), 1),
+            "bf16_mfma_TFLOPs_by_grid": {str(k): round(v, 1) for k, v in mfma.items()},
+            "torch_copy_GBps": round(2 * nbytes / t_copy / 1e9, 1),
+            "torch_bf16_gemm_8192_TFLOPs": round(2 * m ** 3 / t_mm / 1e12, 1),
+            "how": "pkv_probe_stream_read over 4 GiB and pkv_probe_mfma_bf16 (10000 rounds of 4 MFMA chains "
+                   "per wave), best grid; torch copy_ of 4 GiB (read + write) and torch.matmul of two 8192^2 "
+                   "bf16 matrices for reference"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -598,7 +669,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip the smaller decode shapes and the block kernels")
+    ap.add_argument("--no-extra", action="store_true", help="skip the smaller decode shapes, the block kernels and the measured peaks")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (scale for rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -652,6 +723,17 @@ def main():
             print(f"[bench] {k_}: best partition {b_}: {v_['by_partition_size'][b_]}", flush=True)
         blocks = bench_block_ops(args, torch, pkv, workloads)
         print(f"[bench] block ops: {blocks}", flush=True)
+    peaks = None
+    if not args.no_extra:
+        peaks = measured_peaks(torch)
+        print(f"[bench] measured peaks: {peaks}", flush=True)
+        r = d["roofline"]
+        r["measured_peak"] = peaks["hbm_read_GBps"]
+        r["frac_of_measured"] = round(r["achieved"] / peaks["hbm_read_GBps"], 4)
+        for p_ in (pre, pre8):
+            if p_ and "roofline" in p_:
+                p_["roofline"]["measured_peak"] = peaks["bf16_mfma_TFLOPs"]
+                p_["roofline"]["frac_of_measured"] = round(p_["roofline"]["achieved"] / peaks["bf16_mfma_TFLOPs"], 4)
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (fp64 oracle, one thread)...", flush=True)
@@ -691,6 +773,7 @@ def main():
         "mixed_step": mixed,
         "decode_shapes": shapes,
         "block_ops": blocks,
+        "measured_peaks": peaks,
     }
     print(json.dumps(line), flush=True)
 

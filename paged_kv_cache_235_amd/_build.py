@@ -3,7 +3,8 @@
     python -m paged_kv_cache_235_amd._build
 
 Every source is compiled on each call (one hipcc per file, in parallel) and
-linked into ``paged_kv_cache_235_amd/libpagedkv.so``.
+linked into ``paged_kv_cache_235_amd/libpagedkv.so``; the measurement kernels
+of ``include/pkv_probe.h`` go into ``libpkvprobe.so`` beside it.
 """
 from __future__ import annotations
 
@@ -19,10 +20,12 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libpagedkv.so")
+PROBE_LIB_PATH = os.path.join(PKG, "libpkvprobe.so")
 ARCH = "gfx950"
 
 SOURCES = ["pkv_api.cpp", "block_allocator.cpp", "kv_write.hip", "decode.hip", "prefill.hip",
            "block_ops.hip"]
+PROBE_SOURCES = ["peak_probe.hip"]
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 instructions.
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
@@ -46,19 +49,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int | None = None, verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    jobs = jobs or min(len(SOURCES), os.cpu_count() or 1)
-    with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB_PATH + f".tmp{os.getpid()}"
+def _link(objs: list, path: str) -> None:
+    tmp = path + f".tmp{os.getpid()}"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, path)
+
+
+def build(jobs: int | None = None, verbose: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    jobs = jobs or min(len(srcs), os.cpu_count() or 1)
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:len(SOURCES)], LIB_PATH)
+    _link(objs[len(SOURCES):], PROBE_LIB_PATH)
     if verbose:
-        print(f"built {LIB_PATH}")
+        print(f"built {LIB_PATH} and {PROBE_LIB_PATH}")
     return LIB_PATH
 
 

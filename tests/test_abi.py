@@ -14,8 +14,8 @@ PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EWORKSPACE = 0, 1, 2, 3
 F32, BF16, I8 = 1, 2, 4
 
 
-def declared_functions():
-    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+def declared_functions(header=HEADER):
+    text = re.sub(r"/\*.*?\*/", "", open(header).read(), flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\**\s*(\w+)\s*\(", text, flags=re.M)))
 
 
@@ -191,3 +191,28 @@ def test_allocator_abi_rejects_null_and_bad_sizes(lib):
     finally:
         assert lib.pkv_allocator_destroy(h) == PKV_OK
     assert lib.pkv_allocator_destroy(None) == PKV_OK
+
+
+def test_probe_library_exports_its_header_and_rejects_bad_arguments():
+    """The measurement kernels (include/pkv_probe.h) live in a library of their
+    own; bad arguments are refused before any launch."""
+    from paged_kv_cache_235_amd import _build
+    if not os.path.exists(_build.PROBE_LIB_PATH):
+        _build.build()
+    plib = ctypes.CDLL(_build.PROBE_LIB_PATH)
+    names = declared_functions(os.path.join(ROOT, "include", "pkv_probe.h"))
+    assert names == ["pkv_probe_mfma_bf16", "pkv_probe_stream_read"]
+    for n in names:
+        assert hasattr(plib, n), n
+    sr = plib.pkv_probe_stream_read
+    sr.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+    assert sr(FAKE, 15, FAKE, 1, None) == 1          # not whole 16-byte chunks
+    assert sr(FAKE, 0, FAKE, 1, None) == 1
+    assert sr(FAKE, 16, FAKE, 0, None) == 1          # empty grid
+    assert sr(None, 16, FAKE, 1, None) == 1
+    assert sr(ctypes.c_void_p(0x1008), 16, FAKE, 1, None) == 1   # not 16-byte aligned
+    mm = plib.pkv_probe_mfma_bf16
+    mm.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_uint32, ctypes.c_void_p]
+    assert mm(FAKE, -1, 1, 0, None) == 1
+    assert mm(FAKE, 1, 0, 0, None) == 1
+    assert mm(None, 1, 1, 0, None) == 1
