@@ -152,3 +152,14 @@ def test_llama_shaped_full_size_sampled():
     assert_close(out[pick], ref, "bf16", f"sequences {pick}")
     o = out.float()
     assert torch.isfinite(o).all()
+
+
+def test_longest_context_of_the_llama_shaped_range():
+    """Contexts at the top of the Llama-shaped length range (32768 tokens) and
+    one past it, beside one-block ones, with that workload's group of 4 q heads
+    per KV head, head_dim 128 and 512-token partitions: the long rows have 64
+    and 65 partitions, one more than the merge kernel's wave holds at once."""
+    lens = [32768, 32769, 1, 511, 512, 513]
+    case = workloads.make_case("longest", 79, lens, [1] * len(lens), 8, 2, 128)
+    out, _ = _gpu(case, partition_size=512)
+    assert_close(out, expected_outputs(case), "bf16", "part=512")
