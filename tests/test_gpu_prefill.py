@@ -44,6 +44,17 @@ def test_prefill_matches_oracle(lens, new, window):
     assert_close(out, expected_outputs(case), "bf16", f"W={window}")
 
 
+@pytest.mark.parametrize("window", [0, 4096])
+def test_prefill_large_chunk_many_row_tiles(window):
+    """A 1024-token chunk (4096 query rows with 4 q heads per KV head: 16 row
+    tiles of one (sequence, KV head)) on a 4200-token sequence, beside a whole
+    700-token sequence; with the 4096-token window the chunk's early rows see
+    keys from position 0 and its late rows start past it."""
+    case = _case([4200, 700], [1024, 700], window=window, seed=80)
+    out, _ = _gpu(case)
+    assert_close(out, expected_outputs(case), "bf16", f"W={window}")
+
+
 GEOMS = [(4, 4, 128), (8, 2, 64), (12, 2, 128), (6, 1, 64), (32, 8, 128), (16, 2, 128), (5, 5, 64)]
 
 
