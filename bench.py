@@ -591,6 +591,53 @@ def calibrate_copy(torch):
     print(f"[bench] calibration copy: 3 launches, each {n * 4} bytes read and {n * 4} written", flush=True)
 
 
+def bench_kv_write(args, torch, pkv):
+    """kv_cache_write at sizes where bandwidth, not launch latency, decides: the
+    window-4096 prefill step's 4096 new tokens and a 65536-token batch, as bf16
+    copies and as INT8 quantising writes, Llama-shaped heads (8 KV heads,
+    head_dim 128), slots on shuffled blocks.  Algorithmic bytes: the bf16 K and
+    V read once, the pool bytes (and fp16 scales) written once."""
+    dev = torch.device("cuda", 0)
+    hkv, d, bs = 8, 128, 16
+    g = torch.Generator(device=dev).manual_seed(11)
+    res = {}
+    for n in (4096, 65536):
+        nb = n // bs
+        k = torch.randn((n, hkv, d), device=dev, dtype=torch.float32, generator=g).to(torch.bfloat16)
+        v = torch.randn((n, hkv, d), device=dev, dtype=torch.float32, generator=g).to(torch.bfloat16)
+        perm = torch.randperm(nb, device=dev, generator=g).to(torch.int32)
+        slots = (perm[:, None] * bs + torch.arange(bs, device=dev, dtype=torch.int32)[None, :]).reshape(-1)
+        for kv in ("bf16", "i8"):
+            if kv == "bf16":
+                kp = torch.empty((nb, hkv, bs, d), dtype=torch.bfloat16, device=dev)
+                vp = torch.empty_like(kp)
+                ks = vs = None
+                wbytes = 2 * n * hkv * d * 2
+            else:
+                kp = torch.empty((nb, hkv, bs, d), dtype=torch.int8, device=dev)
+                vp = torch.empty_like(kp)
+                ks = torch.empty((nb, hkv, bs), dtype=torch.float16, device=dev)
+                vs = torch.empty_like(ks)
+                wbytes = 2 * n * hkv * (d + 2)
+            nbytes = 2 * n * hkv * d * 2 + wbytes
+            call = lambda: pkv.kv_cache_write(k, v, slots, kp, vp, ks, vs)
+            for _ in range(args.warmup):
+                call()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(args.steps)]
+            for a_, b_ in ev:
+                a_.record()
+                call()
+                b_.record()
+            torch.cuda.synchronize()
+            us = float(np.median([a_.elapsed_time(b_) for a_, b_ in ev])) * 1e3
+            res[f"{kv} pool, {n} tokens"] = {"us_median": round(us, 2), "bytes": nbytes,
+                                             "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1)}
+        del k, v, kp, vp, ks, vs
+    torch.cuda.empty_cache()
+    return res
+
+
 def measured_peaks(torch):
     """What this GPU reaches, beside the published peaks the roofline fractions
     are quoted against.  The measurement kernels of include/pkv_probe.h: a
@@ -711,7 +758,7 @@ def main():
         except pkv.PagedKVError as e:
             pre8 = {"error": str(e)}
         torch.cuda.empty_cache()
-    shapes = blocks = mixed = i8big = None
+    shapes = blocks = mixed = i8big = kvw = None
     if not args.no_extra:
         i8big = bench_decode_int8_large(args, torch, pkv, workloads, tl)
         print(f"[bench] INT8 Llama-shaped decode: {i8big}", flush=True)
@@ -723,6 +770,8 @@ def main():
             print(f"[bench] {k_}: best partition {b_}: {v_['by_partition_size'][b_]}", flush=True)
         blocks = bench_block_ops(args, torch, pkv, workloads)
         print(f"[bench] block ops: {blocks}", flush=True)
+        kvw = bench_kv_write(args, torch, pkv)
+        print(f"[bench] kv_cache_write at scale: {kvw}", flush=True)
     peaks = None
     if not args.no_extra:
         peaks = measured_peaks(torch)
@@ -773,6 +822,7 @@ def main():
         "mixed_step": mixed,
         "decode_shapes": shapes,
         "block_ops": blocks,
+        "kv_cache_write_at_scale": kvw,
         "measured_peaks": peaks,
     }
     print(json.dumps(line), flush=True)
