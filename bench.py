@@ -110,6 +110,46 @@ def write_bytes(num_tokens, num_kv_heads, head_dim, esz=2):
     return 2 * 2 * num_tokens * num_kv_heads * head_dim * esz + 4 * num_tokens
 
 
+def partition_sweep(args, torch, pkv, tl, case, pools, bt, lens, q, sizes, check, ref, part_bytes):
+    """The same resident decode batch at other split-K partition sizes (a choice
+    the caller makes): the partition kernel's time between the library's events
+    on the launch stream, the whole call's time, and a check of each size's
+    output on the sampled sequences."""
+    dev = q.device
+    out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    res = {}
+    for P in sizes:
+        ws = pkv.decode_workspace_size(case.num_seqs, case.num_q_heads, case.head_dim, case.max_blocks_per_seq,
+                                       case.block_size, P)
+        w = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+
+        def call(e=None):
+            if e:
+                pkv.set_decode_start_event(e[1])
+                pkv.set_decode_split_event(e[2])
+                e[0].record()
+            pkv.paged_attention_decode(q, pools["k"], pools["v"], bt, lens, case.softmax_scale, partition_size=P,
+                                       k_scale=pools["ks"], v_scale=pools["vs"], out=out, workspace=w)
+            if e:
+                e[3].record()
+                pkv.set_decode_start_event(None)
+                pkv.set_decode_split_event(None)
+
+        for _ in range(args.warmup):
+            call()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+        for e in ev:
+            call(e)
+        torch.cuda.synchronize()
+        part_us = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e3
+        call_us = float(np.mean([e[0].elapsed_time(e[3]) for e in ev])) * 1e3
+        err = tl.assert_close(out[check], ref, "bf16", f"partition size {P}")
+        gbs = part_bytes / (part_us * 1e-6) / 1e9
+        res[str(P)] = {"partition_us": round(part_us, 1), "call_us": round(call_us, 1), "GB/s": round(gbs, 1),
+                       "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "max_abs_err_sampled": float(err)}
+    return res
+
+
 def bench_decode(args, torch, pkv, workloads, tl):
     dev = torch.device("cuda", 0)
     case = workloads.llama_decode()
@@ -186,7 +226,12 @@ def bench_decode(args, torch, pkv, workloads, tl):
     part_bytes = b["kv"] + b["table"] + b["q"]
     part_s = float(np.mean(t_part)) / 1e3
     achieved = part_bytes / part_s / 1e9
+    sweep = None
+    if not args.no_extra:
+        sweep = partition_sweep(args, torch, pkv, tl, case, pools, bt, lens, q, (512, 1024, 2048), check, ref,
+                                part_bytes)
     return {
+        "partition_size_sweep": sweep,
         "case": case,
         "pools": pools,
         "ms_per_step": total_ms / args.steps,
@@ -357,17 +402,19 @@ def bench_decode_int8_large(args, torch, pkv, workloads, tl):
     check = sorted({int(np.argmax(case.seq_lens)), int(np.argmin(case.seq_lens)), 7})
     sub = case.subset(check)
     from oracle.cases import build_cache, expected_outputs
-    err = tl.assert_close(out[check], expected_outputs(sub, cache=build_cache(sub, device=dev)), "bf16",
-                          "int8 large decode")
+    ref = expected_outputs(sub, cache=build_cache(sub, device=dev))
+    err = tl.assert_close(out[check], ref, "bf16", "int8 large decode")
     b = decode_bytes(case)
     part_bytes = b["kv"] + b["table"] + b["q"]
+    sweep = partition_sweep(args, torch, pkv, tl, case, pools, bt, lens, q, (512, 1024, 2048), check, ref,
+                            part_bytes)
     del pools
     torch.cuda.empty_cache()
     return {"workload": "Llama-3-8B-shaped decode batch (256 seqs, 840,545 tokens) over an INT8 pool",
             "partition_us": round(us, 1), "algorithmic_bytes_per_launch": part_bytes,
             "GB/s": round(part_bytes / (us / 1e6) / 1e9, 1),
             "frac_of_hbm_peak": round(part_bytes / (us / 1e6) / 1e9 / HBM_PEAK_GBS, 4),
-            "max_abs_err_sampled": float(err)}
+            "max_abs_err_sampled": float(err), "partition_size_sweep": sweep}
 
 
 # ------------------------------------------------------------------ mixed step
@@ -813,6 +860,7 @@ def main():
         "roofline": d["roofline"],
         "cpu_baseline": cpu,
         "breakdown_us": d["breakdown_us"],
+        "decode_partition_size_sweep": d["partition_size_sweep"],
         "kv_cache_write": d["kv_cache_write"],
         "algorithmic_bytes": d["bytes"],
         "max_abs_err_sampled": d["max_abs_err"],
