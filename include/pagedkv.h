@@ -3,11 +3,12 @@
  * Instinct MI355X (gfx950).
  *
  * The operation is the serving-engine step the pages describe:
- *   - "PyTorch LLM Serving Engine", section Loading: each layer writes its new
- *     K/V vectors into physical cache slots, then attends with a numerically
- *     stable online softmax while walking the sequence's block table;
- *     section What is implemented: fixed-size physical blocks, per-sequence
- *     block tables, chunked prefill.
+ *   - "PyTorch LLM Serving Engine", section Loading: the new keys and values
+ *     of a layer are stored in the cache first; the attention then visits the
+ *     sequence's blocks in table order with an online softmax (a running
+ *     maximum keeps every exponential bounded); section What is implemented:
+ *     a pool of equal-sized blocks, a block-id table for each sequence,
+ *     prefill in chunks.
  *   - "MicroGen: Modular, Hardware-Aware LLM Inference Engine", section Key
  *     Features: logical-to-physical block mapping, grouped-query attention
  *     (each KV head serves a group of query heads), dynamic per-vector INT8 KV

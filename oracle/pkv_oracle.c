@@ -11,10 +11,12 @@
  * (see quantize_vector), so the bytes it writes are the unique expected bytes.
  *
  * What is computed, and where the pages state it:
- *  - "PyTorch LLM Serving Engine", section Loading: each layer writes its K/V
- *    to a physical cache slot, then runs a numerically stable softmax while
- *    walking the sequence's block table.  Section What is implemented:
- *    fixed-size physical blocks, per-sequence block tables, chunked prefill.
+ *  - "PyTorch LLM Serving Engine", section Loading: in the serving path a
+ *    layer stores the new keys and values in the cache first; its attention
+ *    then visits the sequence's blocks in table order with an online softmax
+ *    (a running maximum keeps the exponentials bounded).  Section What is
+ *    implemented: a cache of equal-sized blocks, a table of block ids per
+ *    sequence, prefill in chunks.
  *  - "MicroGen", section Key Features: logical-to-physical block mapping;
  *    grouped-query attention by repeating each KV head for its group of query
  *    heads; dynamic per-vector INT8 KV quantisation; window-length eviction.
@@ -33,7 +35,10 @@
  *  - a sequence length counts the tokens written by the current step, and a
  *    query at position p sees key j iff j <= p and, with a window W > 0,
  *    j > p - W (W keys including itself);
- *  - INT8: see quantize_vector; an empty context gives a zero output row.
+ *  - INT8: see quantize_vector; an empty context gives a zero output row;
+ *  - a table entry that is not a block of the pool (-1: released by window
+ *    eviction or a rollback) holds no keys, and a query with no key left
+ *    gets a zero output row, like an empty context.
  */
 #include <math.h>
 #include <stdint.h>
@@ -168,8 +173,8 @@ static float input_as_float(const void* base, int32_t dtype, int64_t i)
 
 /*
  * Write each token's K and V vectors into its physical slot ("PyTorch LLM
- * Serving Engine", Loading: K/V are written to a physical cache slot before
- * attending).  Token t's vector for KV head h starts at element
+ * Serving Engine", Loading: new keys and values enter the cache before the
+ * attention reads it).  Token t's vector for KV head h starts at element
  * t * token_stride + h * head_dim of k and v.  The destination of element d is
  *   pool[slot / block_size][h][slot % block_size][d].
  * Same input and pool type: a bit copy.  INT8 pool: quantize_vector per
@@ -222,7 +227,8 @@ int orc_kv_write(int32_t num_blocks, int32_t block_size, int32_t num_kv_heads, i
 /*
  * Slot of every new row of a step ("MicroGen", Key Features: logical blocks
  * map to physical blocks through the sequence's table; "PyTorch LLM Serving
- * Engine", Loading: the new K/V go to a physical cache slot).  Sequence s owns
+ * Engine", Loading: every new key/value vector gets a cache position of its
+ * own).  Sequence s owns
  * rows [cu_q_lens[s], cu_q_lens[s+1]), C_s of them, and holds L_s = seq_lens[s]
  * tokens once they are written, so its row i sits at position p = L_s - C_s + i
  * and goes to
@@ -318,19 +324,23 @@ static double pool_value(const void* pool, const uint16_t* scale, int32_t kv_dty
  * Contiguous K and V of sequence s, KV head g, tokens [0, len): dst[j][d].
  * Token j of the sequence lives in physical block block_table[j / bs] at
  * offset j % bs ("MicroGen", Key Features: logical-to-physical mapping).
+ * A table entry that is not a block of the pool (-1 after window eviction or
+ * a rollback) holds no keys: present[j] is 0 for its tokens (1 otherwise) and
+ * their rows are left NaN, so any use of them would show.
  */
 static void gather(const void* pool, const uint16_t* scale, int32_t kv_dtype, int32_t num_blocks,
                    int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
-                   const int32_t* table_row, int32_t g, int32_t len, double* dst)
+                   const int32_t* table_row, int32_t g, int32_t len, double* dst,
+                   unsigned char* present)
 {
     for (int32_t j = 0; j < len; ++j) {
         int64_t blk = table_row[j / block_size];
         if (blk < 0 || blk >= num_blocks) {
-            /* no block (an entry released by window eviction): these keys are
-               outside every query's window; NaN makes any use of them show */
+            present[j] = 0;
             for (int32_t d = 0; d < head_dim; ++d) dst[(int64_t)j * head_dim + d] = NAN;
             continue;
         }
+        present[j] = 1;
         int64_t vec = (blk * num_kv_heads + g) * block_size + j % block_size;
         for (int32_t d = 0; d < head_dim; ++d)
             dst[(int64_t)j * head_dim + d] = pool_value(pool, scale, kv_dtype, vec, head_dim, d);
@@ -347,33 +357,40 @@ static int32_t first_visible(int32_t p, int32_t window)
 }
 
 /*
- * Softmax attention of one query vector over keys [lo, hi] of contiguous K, V:
+ * Softmax attention of one query vector over the present keys of [lo, hi] of
+ * contiguous K, V:
  *   score_j = scale * sum_d q_d K_jd
  *   out     = sum_j (exp(score_j - m) / Z) V_j,  m = max_j score_j,
  *                                                  Z = sum_j exp(score_j - m)
  * Two passes: the maximum first (numerical stability), then the weights.
- * No visible key gives a zero vector.  weights (optional) gets each weight at
- * its key index, zero elsewhere in [0, wlen).
+ * Keys whose block is missing (present[j] == 0) take no part; no key at all
+ * gives a zero vector.  weights (optional) gets each weight at its key index,
+ * zero elsewhere in [0, wlen).
  */
-static void attend(const double* qv, const double* K, const double* V, int32_t D,
-                   int32_t lo, int32_t hi, double scale, double* scores,
+static void attend(const double* qv, const double* K, const double* V, const unsigned char* present,
+                   int32_t D, int32_t lo, int32_t hi, double scale, double* scores,
                    double* out, double* weights, int32_t wlen)
 {
     for (int32_t d = 0; d < D; ++d) out[d] = 0.0;
     if (weights)
         for (int32_t j = 0; j < wlen; ++j) weights[j] = 0.0;
-    if (hi < lo) return;
 
     double m = -INFINITY;
+    int32_t n = 0;
     for (int32_t j = lo; j <= hi; ++j) {
+        if (!present[j]) continue;
         double dot = 0.0;
         for (int32_t d = 0; d < D; ++d) dot += qv[d] * K[(int64_t)j * D + d];
         scores[j] = scale * dot;
-        if (scores[j] > m) m = scores[j];
+        if (n == 0 || scores[j] > m) m = scores[j];
+        ++n;
     }
+    if (n == 0) return;
     double Z = 0.0;
-    for (int32_t j = lo; j <= hi; ++j) Z += exp(scores[j] - m);
+    for (int32_t j = lo; j <= hi; ++j)
+        if (present[j]) Z += exp(scores[j] - m);
     for (int32_t j = lo; j <= hi; ++j) {
+        if (!present[j]) continue;
         double w = exp(scores[j] - m) / Z;
         if (weights) weights[j] = w;
         for (int32_t d = 0; d < D; ++d) out[d] += w * V[(int64_t)j * D + d];
@@ -421,11 +438,17 @@ int orc_attention(int32_t num_blocks, int32_t block_size, int32_t num_kv_heads, 
         double* V = (double*)malloc(sizeof(double) * ((size_t)L * D + 1));
         double* scores = (double*)malloc(sizeof(double) * ((size_t)L + 1));
         double* qv = (double*)malloc(sizeof(double) * (size_t)D);
-        if (!K || !V || !scores || !qv) { free(K); free(V); free(scores); free(qv); return 2; }
+        unsigned char* present = (unsigned char*)malloc((size_t)L + 1);
+        if (!K || !V || !scores || !qv || !present) {
+            free(K); free(V); free(scores); free(qv); free(present);
+            return 2;
+        }
 
         for (int32_t g = 0; g < num_kv_heads; ++g) {
-            gather(k_pool, k_scale, kv_dtype, num_blocks, block_size, num_kv_heads, D, table_row, g, L, K);
-            gather(v_pool, v_scale, kv_dtype, num_blocks, block_size, num_kv_heads, D, table_row, g, L, V);
+            gather(k_pool, k_scale, kv_dtype, num_blocks, block_size, num_kv_heads, D, table_row, g, L, K,
+                   present);
+            gather(v_pool, v_scale, kv_dtype, num_blocks, block_size, num_kv_heads, D, table_row, g, L, V,
+                   present);
             for (int32_t i = 0; i < C; ++i) {
                 const int64_t row = (int64_t)r0 + i;
                 const int32_t p = L - C + i;
@@ -435,11 +458,11 @@ int orc_attention(int32_t num_blocks, int32_t block_size, int32_t num_kv_heads, 
                         qv[d] = q_value(q, q_dtype, (row * num_q_heads + h) * D + d);
                     double* o = out + (row * num_q_heads + h) * D;
                     double* w = weights ? weights + (row * num_q_heads + h) * weights_stride : NULL;
-                    attend(qv, K, V, D, lo, p, scale, scores, o, w, L);
+                    attend(qv, K, V, present, D, lo, p, scale, scores, o, w, L);
                 }
             }
         }
-        free(K); free(V); free(scores); free(qv);
+        free(K); free(V); free(scores); free(qv); free(present);
     }
     return 0;
 }
@@ -486,7 +509,8 @@ int orc_decode(int32_t num_blocks, int32_t block_size, int32_t num_kv_heads, int
  *   m_k = max score, l_k = sum exp(score - m_k), o_k = sum exp(score - m_k) V_j;
  * merged with M = max_k m_k and w_k = exp(m_k - M):
  *   out = (sum_k w_k o_k) / (sum_k w_k l_k).
- * Partitions without a visible key take no part.
+ * Partitions without a visible key (none in range, or all in missing blocks)
+ * take no part; a row with none at all is zero.
  */
 int orc_decode_split(int32_t num_blocks, int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
                      int32_t kv_dtype, const void* q, int32_t q_dtype, int32_t num_seqs,
@@ -508,10 +532,16 @@ int orc_decode_split(int32_t num_blocks, int32_t block_size, int32_t num_kv_head
         double* qv = (double*)malloc(sizeof(double) * (size_t)D);
         double* acc = (double*)malloc(sizeof(double) * (size_t)D);
         double* ok = (double*)malloc(sizeof(double) * (size_t)D);
-        if (!K || !V || !qv || !acc || !ok) { free(K); free(V); free(qv); free(acc); free(ok); return 2; }
+        unsigned char* present = (unsigned char*)malloc((size_t)L + 1);
+        if (!K || !V || !qv || !acc || !ok || !present) {
+            free(K); free(V); free(qv); free(acc); free(ok); free(present);
+            return 2;
+        }
         for (int32_t g = 0; g < num_kv_heads; ++g) {
-            gather(k_pool, k_scale, kv_dtype, num_blocks, block_size, num_kv_heads, D, table_row, g, L, K);
-            gather(v_pool, v_scale, kv_dtype, num_blocks, block_size, num_kv_heads, D, table_row, g, L, V);
+            gather(k_pool, k_scale, kv_dtype, num_blocks, block_size, num_kv_heads, D, table_row, g, L, K,
+                   present);
+            gather(v_pool, v_scale, kv_dtype, num_blocks, block_size, num_kv_heads, D, table_row, g, L, V,
+                   present);
             const int32_t p = L - 1;
             const int32_t lo = first_visible(p, window);
             for (int32_t h = g * G; h < (g + 1) * G; ++h) {
@@ -522,6 +552,7 @@ int orc_decode_split(int32_t num_blocks, int32_t block_size, int32_t num_kv_head
                 for (int32_t k0 = 0; k0 < L; k0 += partition_size) {
                     int32_t a = k0 > lo ? k0 : lo, b = (k0 + partition_size - 1 < p) ? k0 + partition_size - 1 : p;
                     for (int32_t j = a; j <= b; ++j) {
+                        if (!present[j]) continue;
                         double dot = 0.0;
                         for (int32_t d = 0; d < D; ++d) dot += qv[d] * K[(int64_t)j * D + d];
                         if (scale * dot > M) M = scale * dot;   /* max over all = max of partition maxima */
@@ -531,15 +562,19 @@ int orc_decode_split(int32_t num_blocks, int32_t block_size, int32_t num_kv_head
                 for (int32_t d = 0; d < D; ++d) acc[d] = 0.0;
                 for (int32_t k0 = 0; k0 < L; k0 += partition_size) {
                     int32_t a = k0 > lo ? k0 : lo, b = (k0 + partition_size - 1 < p) ? k0 + partition_size - 1 : p;
-                    if (b < a) continue;
                     double mk = -INFINITY, lk = 0.0;
+                    int32_t n = 0;
                     for (int32_t j = a; j <= b; ++j) {
+                        if (!present[j]) continue;
                         double dot = 0.0;
                         for (int32_t d = 0; d < D; ++d) dot += qv[d] * K[(int64_t)j * D + d];
-                        if (scale * dot > mk) mk = scale * dot;
+                        if (n == 0 || scale * dot > mk) mk = scale * dot;
+                        ++n;
                     }
+                    if (n == 0) continue;
                     for (int32_t d = 0; d < D; ++d) ok[d] = 0.0;
                     for (int32_t j = a; j <= b; ++j) {
+                        if (!present[j]) continue;
                         double dot = 0.0;
                         for (int32_t d = 0; d < D; ++d) dot += qv[d] * K[(int64_t)j * D + d];
                         double e = exp(scale * dot - mk);
@@ -553,7 +588,7 @@ int orc_decode_split(int32_t num_blocks, int32_t block_size, int32_t num_kv_head
                 for (int32_t d = 0; d < D; ++d) o[d] = (num_l > 0.0) ? acc[d] / num_l : 0.0;
             }
         }
-        free(K); free(V); free(qv); free(acc); free(ok);
+        free(K); free(V); free(qv); free(acc); free(ok); free(present);
     }
     return 0;
 }

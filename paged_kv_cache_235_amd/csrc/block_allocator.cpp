@@ -1,8 +1,8 @@
 // block_allocator.cpp -- host-side owner of a pool's physical blocks and the
-// edits of per-sequence block tables that allocation implies.
+// table edits that allocation implies.
 //
-// "PyTorch LLM Serving Engine", What is implemented: fixed-size physical
-// blocks handed to sequences through per-sequence block tables.  "MicroGen",
+// "PyTorch LLM Serving Engine", What is implemented: the pool is cut into
+// blocks of one size, and each sequence lists the blocks it holds in a table.  "MicroGen",
 // Key Features: logical-to-physical block mapping, window-length eviction for
 // long contexts, prefix sharing and KV rollback for speculative decoding.
 //

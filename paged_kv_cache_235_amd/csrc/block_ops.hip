@@ -3,9 +3,9 @@
 // sequences.
 //
 // "MicroGen", Key Features: logical blocks map to physical blocks through the
-// sequence's table; "PyTorch LLM Serving Engine", Loading: each new K/V
-// vector is written to a physical cache slot, and What is implemented:
-// per-sequence block tables over fixed-size blocks.
+// sequence's table; "PyTorch LLM Serving Engine", Loading (new keys and
+// values are stored before attention) and What is implemented (a block-id
+// table for each sequence, blocks of one size).
 //
 // Slot mapping: one workgroup per sequence walks its rows (a decode step has
 // one, a prefill chunk hundreds); each row reads one table entry.  Block copy:

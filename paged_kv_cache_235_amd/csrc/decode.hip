@@ -1,8 +1,8 @@
 // decode.hip -- paged attention for one query token per sequence.
 //
-// "PyTorch LLM Serving Engine", Loading and What is implemented: attend while
-// walking the sequence's block table with a numerically stable online
-// softmax.  "MicroGen", Key Features: grouped-query attention (every KV head
+// "PyTorch LLM Serving Engine", Loading and What is implemented: the query
+// visits the sequence's cache blocks in table order and keeps a running
+// maximum, so the softmax (an online one) never overflows.  "MicroGen", Key Features: grouped-query attention (every KV head
 // serves G query heads), dynamic INT8 KV, window-length limit.
 //
 // Work decomposition (gfx950, wave64):

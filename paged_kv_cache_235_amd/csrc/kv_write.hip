@@ -1,7 +1,7 @@
-// kv_write.hip -- store new K/V vectors in their physical cache slots.
+// kv_write.hip -- store new K/V vectors at their slots in the block pool.
 //
-// "PyTorch LLM Serving Engine", Loading: K/V are written to a physical cache
-// slot, then attended.  "MicroGen", Key Features: dynamic per-vector INT8 KV.
+// "PyTorch LLM Serving Engine", Loading: the cache receives the new keys and
+// values before attention runs.  "MicroGen", Key Features: dynamic per-vector INT8 KV.
 //
 // Copy path: one thread per 16-byte chunk of a (token, head) vector, K and V
 // handled by the same thread; loads and stores are 16 B wide and a wave moves

@@ -1,10 +1,10 @@
 // prefill.hip -- paged attention for a chunk of new query tokens per sequence
 // (chunked prefill) on bf16 MFMA.
 //
-// "PyTorch LLM Serving Engine", What is implemented: prefill runs in
-// configurable chunks that share the step with decode work; Loading: the
-// chunk's K/V are written to their cache slots first, then the chunk attends
-// over the block table with a stable online softmax.  "MicroGen", Key
+// "PyTorch LLM Serving Engine", What is implemented: prefill is cut into
+// chunks of a chosen size that run in the same engine step as decode rows;
+// Loading: the chunk's keys and values are stored first, then its queries
+// visit the block table with an online (running-maximum) softmax.  "MicroGen", Key
 // Features: grouped-query heads, window-length limit.
 //
 // Many query rows make Q.K^T and P.V dense contractions, so they run on

@@ -131,12 +131,40 @@ def test_copied_blocks_attend_identically():
     assert np.array_equal(got, ref)
 
 
+def _sdpa_rows_with_absent_blocks(case, s, absent_cols):
+    """Dense fp64 attention (torch SDPA) of sequence s's query rows over its
+    generated K/V, causal and windowed, with the keys of the logical blocks in
+    absent_cols removed from every row; rows with no key left are zero."""
+    L, C = int(case.seq_lens[s]), int(case.new_lens[s])
+    W = case.window
+    q = case.q_seq(s).double().permute(1, 0, 2).unsqueeze(0)
+    k = case.kv("k", s, 0, L).double().permute(1, 0, 2).unsqueeze(0)
+    v = case.kv("v", s, 0, L).double().permute(1, 0, 2).unsqueeze(0)
+    pos = torch.arange(L - C, L)[:, None]
+    key = torch.arange(L)[None, :]
+    mask = key <= pos
+    if W > 0:
+        mask &= key > pos - W
+    present = torch.ones(L, dtype=torch.bool)
+    for c in absent_cols:
+        present[c * 16:(c + 1) * 16] = False
+    mask &= present[None, :]
+    empty = ~mask.any(1)
+    mask[empty, 0] = True                       # SDPA needs a key per row; those rows are zeroed below
+    ref = F.scaled_dot_product_attention(q, k, v, attn_mask=mask, scale=float(case.softmax_scale),
+                                         enable_gqa=True)[0].permute(1, 0, 2).numpy()
+    ref[empty.numpy()] = 0.0
+    return ref
+
+
 @pytest.mark.parametrize("kind", ["decode", "prefill"])
 def test_missing_blocks_before_the_window_change_nothing(kind):
     """Window eviction releases the blocks wholly before every query's window and
     marks their table entries -1 ("MicroGen", Key Features: window-length
-    eviction); the oracle must give the same output without reading them, and
-    NaN if a query could see such a block."""
+    eviction); the oracle must give the same output without reading them.  A
+    released block that a query could still see holds no keys for it: the
+    output is attention over the keys that remain (torch SDPA with that
+    block's keys masked out)."""
     W = 40
     lens, new = [300, 97, 64], ([1, 1, 1] if kind == "decode" else [20, 30, 64])
     case = workloads.make_case("evict", 64, lens, new, 8, 2, 64, window=W, kind=kind)
@@ -150,11 +178,46 @@ def test_missing_blocks_before_the_window_change_nothing(kind):
     assert (evicted == -1).any()
     case.block_tables = evicted
     assert np.array_equal(expected_outputs(case, cache=cache), ref)
-    # one more block, still inside a window: the output shows it
+    # one more block, still inside a window: the rows that saw it now attend
+    # over the remaining keys only
     s = 0
     first_query = int(case.seq_lens[s]) - int(case.new_lens[s])
-    evicted[s, max(0, first_query - W + 1) // 16] = -1
-    assert np.isnan(expected_outputs(case, cache=cache)[case.cu_q_lens[s]]).all()
+    col = max(0, first_query - W + 1) // 16
+    evicted[s, col] = -1
+    got = expected_outputs(case, cache=cache)
+    cu = case.cu_q_lens
+    sdpa = _sdpa_rows_with_absent_blocks(case, s, [col])
+    np.testing.assert_allclose(got[cu[s]:cu[s + 1]], sdpa, rtol=0, atol=1e-12)
+    assert not np.allclose(got[cu[s]:cu[s + 1]], ref[cu[s]:cu[s + 1]])
+
+
+@pytest.mark.parametrize("kind", ["decode", "prefill"])
+def test_entries_without_a_block_hold_no_keys(kind):
+    """A table entry that is not a block of the pool (-1, or an id past the pool)
+    inside the visible range holds no keys: the oracle equals dense attention
+    over the keys that remain, and a row left with no key is zero (like an
+    empty context).  Covers single and split-K decode."""
+    lens = [100, 40, 33, 16]
+    new = [1] * 4 if kind == "decode" else [30, 40, 10, 16]
+    case = workloads.make_case("absent", 65, lens, new, 8, 2, 64, kind=kind)
+    cache = build_cache(case)
+    holes = {0: [1, 3], 1: [0], 2: [2], 3: [0]}        # sequence 3 loses its only block
+    t = case.block_tables.copy()
+    for s, cols in holes.items():
+        for c in cols:
+            t[s, c] = -1 if c % 2 == 0 else case.num_blocks + 5
+    case.block_tables = t
+    got = expected_outputs(case, cache=cache)
+    cu = case.cu_q_lens
+    for s, cols in holes.items():
+        np.testing.assert_allclose(got[cu[s]:cu[s + 1]], _sdpa_rows_with_absent_blocks(case, s, cols),
+                                   rtol=0, atol=1e-12)
+    assert (got[cu[3]:cu[4]] == 0).all()
+    if kind == "decode":
+        q = to_numpy(case.q())
+        for part in (16, 32):
+            split = oracle.decode_split(cache, q, case.in_dtype, case.seq_lens, t, case.softmax_scale, part)
+            np.testing.assert_allclose(split, got, rtol=0, atol=1e-12)
 
 
 def test_logical_tables_of_offset_rows():

@@ -46,11 +46,14 @@ MUTANTS = [
      [N.test_f32_to_f16_ties_go_to_even]),
     ("chunk rows at the wrong position", "const int32_t p = L - C + i;", "const int32_t p = i;",
      [lambda: P.test_each_chunk_row_equals_decode_over_its_prefix(0)]),
-    ("no causal mask inside a chunk", "attend(qv, K, V, D, lo, p, scale, scores, o, w, L);",
-     "attend(qv, K, V, D, lo, L - 1, scale, scores, o, w, L);",
+    ("no causal mask inside a chunk", "attend(qv, K, V, present, D, lo, p, scale, scores, o, w, L);",
+     "attend(qv, K, V, present, D, lo, L - 1, scale, scores, o, w, L);",
      [lambda: P.test_whole_sequence_chunk_equals_causal_sdpa("bf16")]),
     ("merge weights dropped", "double wk = exp(mk - M);", "double wk = 1.0;",
      [lambda: A.test_split_partitions_merge_to_the_two_pass_result(64, 0)]),
+    ("keys of missing blocks kept", "        if (!present[j]) continue;\n        double dot = 0.0;\n        for (int32_t d = 0; d < D; ++d) dot += qv[d] * K[(int64_t)j * D + d];\n        scores[j] = scale * dot;",
+     "        double dot = 0.0;\n        for (int32_t d = 0; d < D; ++d) dot += qv[d] * K[(int64_t)j * D + d];\n        scores[j] = scale * dot;",
+     [lambda: BL.test_entries_without_a_block_hold_no_keys("prefill")]),
     ("slot one position late", "int64_t p = (int64_t)seq_lens[s] - (r1 - r0) + (r - r0);",
      "int64_t p = (int64_t)seq_lens[s] - (r1 - r0) + (r - r0) + 1;",
      [BL.test_slot_mapping_round_trip_equals_dense_causal_attention,

@@ -7,7 +7,7 @@ binding nor the reference implementation, so both can be fed from it.
 
 Shapes follow the serving workloads on the pages:
 
-* fixed 16-token physical blocks with per-sequence block tables
+* 16-token blocks, addressed through a block-id table per sequence
   ("PyTorch LLM Serving Engine", §What is implemented; "llminfer",
   §Paged KV Cache And Continuous Batching, page_size_tokens = 16);
 * right-skewed, clipped log-normal context lengths ("PyTorch LLM Serving
