@@ -119,9 +119,8 @@ def partition_sweep(args, torch, pkv, tl, case, pools, bt, lens, q, sizes, check
     out = torch.empty(q.shape, dtype=torch.float32, device=dev)
     res = {}
     for P in sizes:
-        ws = pkv.decode_workspace_size(case.num_seqs, case.num_q_heads, case.head_dim, case.max_blocks_per_seq,
-                                       case.block_size, P)
-        w = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+        w = pkv.decode_workspace(case.num_seqs, case.num_q_heads, case.head_dim, case.max_blocks_per_seq,
+                                 case.block_size, P, device=dev)
 
         def call(e=None):
             if e:
@@ -163,9 +162,9 @@ def bench_decode(args, torch, pkv, workloads, tl):
     new_v = case.kv_at("v", case.new_tokens(), dev)
     new_slots = torch.from_numpy(case.new_slots()).to(dev)
     out = torch.empty(q.shape, dtype=torch.float32, device=dev)
-    ws_bytes = pkv.decode_workspace_size(case.num_seqs, case.num_q_heads, case.head_dim,
-                                         case.max_blocks_per_seq, case.block_size, case.partition_size)
-    workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    workspace = pkv.decode_workspace(case.num_seqs, case.num_q_heads, case.head_dim, case.max_blocks_per_seq,
+                                     case.block_size, case.partition_size, device=dev)
+    ws_bytes = workspace.numel()
     torch.cuda.synchronize()
     print(f"[bench] decode setup done; workspace {ws_bytes / 2**20:.1f} MiB", flush=True)
 
@@ -208,9 +207,10 @@ def bench_decode(args, torch, pkv, workloads, tl):
     torch.cuda.synchronize()
     REGIONS.pause()
     t_write = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    t_reset = np.array([e[1].elapsed_time(e[2]) for e in evs])     # work-counter clear + launch gap
+    t_gap = np.array([e[1].elapsed_time(e[2]) for e in evs])       # between the write and the partition kernel
     t_part = np.array([e[2].elapsed_time(e[3]) for e in evs])
     t_merge = np.array([e[3].elapsed_time(e[4]) for e in evs])
+    t_call = np.array([e[2].elapsed_time(e[4]) for e in evs])      # the decode call: partition + merge
     t_step = np.array([e[0].elapsed_time(e[4]) for e in evs])
 
     # correctness of the timed configuration, on a sample of sequences
@@ -226,6 +226,8 @@ def bench_decode(args, torch, pkv, workloads, tl):
     part_bytes = b["kv"] + b["table"] + b["q"]
     part_s = float(np.mean(t_part)) / 1e3
     achieved = part_bytes / part_s / 1e9
+    call_s = float(np.mean(t_call)) / 1e3
+    call_achieved = part_bytes / call_s / 1e9
     sweep = None
     if not args.no_extra:
         sweep = partition_sweep(args, torch, pkv, tl, case, pools, bt, lens, q, (512, 1024, 2048), check, ref,
@@ -234,13 +236,15 @@ def bench_decode(args, torch, pkv, workloads, tl):
         "partition_size_sweep": sweep,
         "case": case,
         "pools": pools,
+        "out": out,
         "ms_per_step": total_ms / args.steps,
         "wall_ms_per_step": wall * 1e3 / args.steps,
         "step_bytes": step_bytes,
         "breakdown_us": {"kv_cache_write": float(np.mean(t_write)) * 1e3,
-                         "decode_counter_clear": float(np.mean(t_reset)) * 1e3,
+                         "write_to_partition_gap": float(np.mean(t_gap)) * 1e3,
                          "decode_partition": float(np.mean(t_part)) * 1e3,
                          "decode_merge": float(np.mean(t_merge)) * 1e3,
+                         "decode_call": float(np.mean(t_call)) * 1e3,
                          "step_median": float(np.median(t_step)) * 1e3,
                          "step_p10": float(np.percentile(t_step, 10)) * 1e3,
                          "step_p90": float(np.percentile(t_step, 90)) * 1e3},
@@ -253,8 +257,60 @@ def bench_decode(args, torch, pkv, workloads, tl):
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": read_traffic("decode_llama3_8b_shaped", "decode.hip"),
                      "algorithmic_bytes_per_launch": part_bytes},
+        # the whole decode call (partition kernel + merge kernel, from the event
+        # before the partition kernel to the one after the call), same bytes
+        "roofline_call": {"what": "paged_attention_decode call: partition + merge kernels", "bound": "hbm",
+                          "achieved": round(call_achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(call_achieved / HBM_PEAK_GBS, 4), "us": round(call_s * 1e6, 1),
+                          "algorithmic_bytes_per_call": part_bytes},
         "max_abs_err": float(err),
     }
+
+
+def full_output_parity(tl, out, ref):
+    """Every output element of the timed decode call against the oracle: the
+    the benchmark spec tolerances asserted, the worst errors reported."""
+    g = out.detach().float().cpu().double().numpy().reshape(ref.shape)
+    err = np.abs(g - ref)
+    dim = ref.shape[-1]
+    e = err.reshape(-1, dim).max(1)
+    r = np.abs(ref).reshape(-1, dim).max(1)
+    rel = float((e[r > 0] / r[r > 0]).max()) if (r > 0).any() else 0.0
+    tl.assert_close(out, ref, "bf16", "whole Llama-shaped decode output")
+    return {"rows": int(ref.shape[0] * ref.shape[1]), "max_abs_err": float(err.max()),
+            "max_per_vector_rel_err": rel, "tolerance": {"abs": tl.ABS_BF16, "per_vector_rel": tl.REL_BF16}}
+
+
+def run_metadata(torch):
+    """ROCm version, GPU, library source hash (and git revision where a checkout
+    is present), and the seed of every workload the line reports."""
+    import subprocess
+    rocm = None
+    for path in ("/opt/rocm/.info/version", "/opt/rocm/.info/version-dev"):
+        try:
+            rocm = open(path).read().strip()
+            break
+        except OSError:
+            continue
+    props = torch.cuda.get_device_properties(0)
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "paged_kv_cache_235_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        h.update(name.encode())
+        h.update(open(os.path.join(csrc, name), "rb").read())
+    h.update(open(os.path.join(ROOT, "include", "pagedkv.h"), "rb").read())
+    rev = None
+    try:
+        rev = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True, text=True,
+                             timeout=10).stdout.strip() or None
+    except (OSError, subprocess.SubprocessError):
+        pass
+    return {"rocm": rocm, "torch": torch.__version__, "gpu": props.name,
+            "gcn_arch": getattr(props, "gcnArchName", None), "compute_units": props.multi_processor_count,
+            "library_source_sha256_16": h.hexdigest()[:16], "git_rev": rev,
+            "seeds": {"llama3-8b-decode": 3, "prefill-window": 5, "qwen2.5-1.5b-decode": 2,
+                      "int8-kv-decode": 4, "tiny-fp32-decode": 1, "mixed-step": 6,
+                      "kv_cache_write_at_scale": 11}}
 
 
 def host_cpu():
@@ -279,8 +335,8 @@ def cpu_baseline(case, torch, dev):
     cache = build_cache(case, device=dev)
     q = to_numpy(case.q())
     t0 = time.perf_counter()
-    oracle.decode(cache, q, case.in_dtype, case.seq_lens, case.block_tables, case.softmax_scale,
-                  case.window)
+    ref = oracle.decode(cache, q, case.in_dtype, case.seq_lens, case.block_tables, case.softmax_scale,
+                        case.window)
     dt = time.perf_counter() - t0
     kv = decode_bytes(case)
     step_bytes = sum(kv.values()) + write_bytes(case.num_seqs, case.num_kv_heads, case.head_dim)
@@ -288,7 +344,7 @@ def cpu_baseline(case, torch, dev):
             "seconds": round(dt, 3), "host": host_cpu(),
             "sample": f"the whole decode step: all {case.num_seqs} sequences, "
                       f"{int(case.seq_lens.sum())} context tokens, gather + two-pass fp64 attention "
-                      f"on one host thread"}
+                      f"on one host thread"}, ref
 
 
 # ------------------------------------------------------------------ prefill
@@ -374,9 +430,8 @@ def bench_decode_int8_large(args, torch, pkv, workloads, tl):
     bt, lens, _ = tl.tables(case, dev)
     q = case.q(dev)
     out = torch.empty(q.shape, dtype=torch.float32, device=dev)
-    ws = pkv.decode_workspace_size(case.num_seqs, case.num_q_heads, case.head_dim, case.max_blocks_per_seq,
-                                   case.block_size, case.partition_size)
-    workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
+    workspace = pkv.decode_workspace(case.num_seqs, case.num_q_heads, case.head_dim, case.max_blocks_per_seq,
+                                     case.block_size, case.partition_size, device=dev)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
 
     def call(e=None):
@@ -433,9 +488,8 @@ def bench_mixed(args, torch, pkv, workloads, tl):
     rows_pf = int(case.cu_q_lens[npf])
     out = torch.empty(q.shape, dtype=torch.float32, device=dev)
     out2 = torch.empty(q.shape, dtype=torch.float32, device=dev)
-    ws = pkv.decode_workspace_size(case.num_seqs - npf, case.num_q_heads, case.head_dim, case.max_blocks_per_seq,
-                                   case.block_size, 512)
-    workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
+    workspace = pkv.decode_workspace(case.num_seqs - npf, case.num_q_heads, case.head_dim, case.max_blocks_per_seq,
+                                     case.block_size, 512, device=dev)
     cu_pf = cu[:npf + 1].contiguous()
 
     def one():
@@ -530,9 +584,8 @@ def bench_decode_shapes(args, torch, pkv, workloads, tl):
         entry = {"workload": name, "context_tokens": int(case.seq_lens.sum()), "algorithmic_bytes": nbytes,
                  "by_partition_size": {}}
         for part in (64, 128, 256, 512):
-            ws = pkv.decode_workspace_size(case.num_seqs, case.num_q_heads, case.head_dim,
-                                           case.max_blocks_per_seq, case.block_size, part)
-            workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+            workspace = pkv.decode_workspace(case.num_seqs, case.num_q_heads, case.head_dim,
+                                             case.max_blocks_per_seq, case.block_size, part, device=dev)
 
             def call():
                 pkv.paged_attention_decode(q, pools["k"], pools["v"], bt, lens, case.softmax_scale,
@@ -831,10 +884,15 @@ def main():
                 p_["roofline"]["measured_peak"] = peaks["bf16_mfma_TFLOPs"]
                 p_["roofline"]["frac_of_measured"] = round(p_["roofline"]["achieved"] / peaks["bf16_mfma_TFLOPs"], 4)
     cpu = None
+    full_parity = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (fp64 oracle, one thread)...", flush=True)
-        cpu = cpu_baseline(case, torch, torch.device("cuda", 0))
+        cpu, ref_all = cpu_baseline(case, torch, torch.device("cuda", 0))
         print(f"[bench] cpu baseline: {cpu['seconds']} s", flush=True)
+        # the timed decode output of the whole batch against the oracle's
+        full_parity = full_output_parity(tl, d["out"], ref_all)
+        print(f"[bench] whole decode output vs oracle: {full_parity}", flush=True)
+    d.pop("out")
     value = d["step_bytes"] / (d["ms_per_step"] / 1e3) / 1e9
     line = {
         "metric": METRIC,
@@ -858,7 +916,10 @@ def main():
                    "context_len_max": int(case.seq_lens.max()), "num_blocks": case.num_blocks,
                    "partition_size": case.partition_size},
         "roofline": d["roofline"],
+        "roofline_call": d["roofline_call"],
         "cpu_baseline": cpu,
+        "full_output_parity": full_parity,
+        "run": run_metadata(torch),
         "breakdown_us": d["breakdown_us"],
         "decode_partition_size_sweep": d["partition_size_sweep"],
         "kv_cache_write": d["kv_cache_write"],

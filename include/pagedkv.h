@@ -79,8 +79,9 @@ typedef struct {
 
 /*
  * kv_cache_write -- store new K/V vectors in their physical slots.
- * ("PyTorch LLM Serving Engine", Loading: K/V are written to a physical cache
- * slot before attention; "MicroGen", Key Features: dynamic per-vector INT8.)
+ * ("PyTorch LLM Serving Engine", Loading: new keys and values enter the cache
+ * before attention reads them; "MicroGen", Key Features: dynamic per-vector
+ * INT8.)
  *
  *   k, v          [num_tokens][num_kv_heads][head_dim] of in_dtype, consecutive
  *                 tokens token_stride elements apart (>= num_kv_heads*head_dim
@@ -119,16 +120,19 @@ size_t paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_q_hea
 
 /*
  * paged_attention_decode -- one query token per sequence.
- * ("PyTorch LLM Serving Engine", Loading and What is implemented: online
- * softmax while walking the sequence's block table; "MicroGen", Key Features:
- * GQA by KV-head repetition, window-length limit.)
+ * ("PyTorch LLM Serving Engine", Loading and What is implemented: an online
+ * softmax over the sequence's blocks in table order; "MicroGen", Key
+ * Features: GQA by KV-head repetition, window-length limit.)
  *
  * For sequence s with L = context_lens[s] tokens (the current token, already
  * written by kv_cache_write, included) and query head h, with
  * G = num_q_heads / cache->num_kv_heads and g = h / G:
  *     p = L - 1;  keys j with 0 <= j <= p and, if sliding_window W > 0, j > p - W
  *     out[s][h] = sum_j softmax_j(softmax_scale * q[s][h] . K_s[j][g]) V_s[j][g]
- * where K_s[j] is the pool row at sequence position j.  L == 0 gives a zero row.
+ * where K_s[j] is the pool row at sequence position j.  A table entry that is
+ * not a block of the pool (-1 after eviction or rollback, or an id outside
+ * [0, num_blocks)) holds no keys: its positions take no part in the softmax.
+ * L == 0, or no key left at all, gives a zero row.
  *
  *   q             [num_seqs][num_q_heads][head_dim]; BF16 for BF16 pools,
  *                 F32 for F32 pools, BF16 or F32 for INT8 pools.
@@ -152,13 +156,16 @@ size_t paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_q_hea
  *                 second kernel (log-sum-exp), which needs `workspace`.
  *   workspace     device scratch of at least
  *                 paged_attention_decode_workspace_size(...) bytes, 256-byte
- *                 aligned; may be NULL when that size is 0.  Its contents need
- *                 no initialisation and are not preserved: when the batch can
- *                 hold more work items than the GPU runs at once, the call
- *                 clears its work counter (first 256 bytes) with a kernel on
- *                 `stream` before use (so the call can be captured in a
- *                 graph); smaller batches use no counter.  Two calls in
- *                 flight at once must not share a workspace.
+ *                 aligned; may be NULL when that size is 0.  Its first 256
+ *                 bytes hold a work counter that must be ZERO before the
+ *                 first call that uses the workspace (allocate it zeroed);
+ *                 every call leaves the counter at zero again when its work
+ *                 completes, so a workspace can be reused call after call
+ *                 with no clearing (and no extra launch, so the call can be
+ *                 captured in a graph).  The rest holds split-K partial
+ *                 results, not preserved between calls.  With
+ *                 PKV_VALIDATE=1 a non-zero counter is rejected (PKV_EINVAL).
+ *                 Two calls in flight at once must not share a workspace.
  * num_seqs == 0 is a no-op.  out must not alias any input or the workspace.
  */
 int paged_attention_decode(const pkv_cache_desc* cache,
@@ -199,10 +206,20 @@ int paged_attention_decode(const pkv_cache_desc* cache,
  *   table_offsets NULL, or per-sequence offsets as for decode.
  *   k_scale/v_scale  INT8 pools only (16-byte aligned), else NULL.
  * Pools are BF16 or INT8 ("MicroGen", Key Features: dynamic per-vector INT8
- * KV).  INT8 keys enter the scores exactly (code . q times the key's scale);
- * each V scale is folded into its key's softmax weight, carried in two fp16
- * parts (~22 significant bits).  Weights reach 256 before a rescale, so V
- * scales must be <= 255 (|values| <= 32385).
+ * KV).  Q.K^T is exact in both (bf16 products, fp32 sums); P.V runs on fp16
+ * matrix instructions with fp32 accumulation, which sets two range limits:
+ *   - BF16 pools: V is converted to fp16 for P.V.  V values must satisfy
+ *     |v| <= 65504 (a larger value becomes inf and the row's output is not
+ *     finite).  Values with |v| < 2^-14 land on fp16's subnormal grid: each
+ *     is off by at most 2^-25 in absolute terms (so the output's absolute
+ *     error bound holds, but an output made only of such values can exceed
+ *     the 1e-2 relative bound).  Values in between convert exactly.
+ *   - INT8 pools: codes are exact in fp16; each V scale is folded into its
+ *     key's softmax weight, carried in two fp16 parts (~22 significant
+ *     bits).  Weights reach 256 before a rescale, so V scales must be <= 255
+ *     (|values| <= 32385).
+ * The decode call has neither limit (its products run in fp32).
+ * A table entry that holds no block holds no keys, as for decode.
  * num_seqs == 0 or max_q_len == 0 is a no-op.
  */
 int paged_attention_prefill_chunk(const pkv_cache_desc* cache,
@@ -222,8 +239,8 @@ int paged_attention_prefill_chunk(const pkv_cache_desc* cache,
  * pkv_build_slot_mapping -- the cache slot of every new row of a step, on the
  * device, from the block tables.
  * ("MicroGen", Key Features: logical blocks map to physical blocks through the
- * sequence's table; "PyTorch LLM Serving Engine", Loading: each new K/V vector
- * goes to a physical cache slot.)
+ * sequence's table; "PyTorch LLM Serving Engine", Loading: every new key/value
+ * vector has a cache position of its own.)
  *
  * Sequence s owns rows [cu_q_lens[s], cu_q_lens[s+1]) (C_s of them: 1 for a
  * decode step, the chunk length for prefill) and holds L_s = seq_lens[s]
@@ -266,8 +283,8 @@ int kv_cache_copy_blocks(const pkv_cache_desc* cache, void* k_pool, void* v_pool
 
 /*
  * Block allocator -- host-side owner of a pool's physical blocks ("PyTorch LLM
- * Serving Engine", What is implemented: fixed-size physical blocks handed out
- * through per-sequence block tables).  Free blocks are kept on a stack (O(1)
+ * Serving Engine", What is implemented: the pool is cut into blocks of one
+ * size, and each sequence lists its blocks in a table).  Free blocks are kept on a stack (O(1)
  * per block); every block carries a reference count so that sequences can
  * share blocks (a forked prefix) and a block is free again when its count
  * drops to zero.  The allocator touches no device memory: table rows are HOST

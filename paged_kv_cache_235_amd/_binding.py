@@ -196,6 +196,17 @@ def decode_workspace_size(num_seqs: int, num_q_heads: int, head_dim: int, max_bl
         num_seqs, num_q_heads, head_dim, max_blocks_per_seq, block_size, partition_size, int(bool(with_table_offsets))))
 
 
+def decode_workspace(num_seqs: int, num_q_heads: int, head_dim: int, max_blocks_per_seq: int,
+                     block_size: int = 16, partition_size: int = 512, with_table_offsets: bool = False,
+                     device=None) -> torch.Tensor:
+    """A decode workspace ready for its first call: at least 256 bytes, all zero
+    (the work counter in its first bytes must start at zero; each call leaves it
+    at zero again)."""
+    n = decode_workspace_size(num_seqs, num_q_heads, head_dim, max_blocks_per_seq, block_size, partition_size,
+                              with_table_offsets)
+    return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
+
+
 def _offsets(t, b, what="table_offsets"):
     if t is None:
         return None
@@ -205,14 +216,8 @@ def _offsets(t, b, what="table_offsets"):
     return t
 
 
-def paged_attention_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
-                           block_tables: torch.Tensor, context_lens: torch.Tensor, softmax_scale: float,
-                           sliding_window: int = 0, partition_size: int = 512,
-                           k_scale: torch.Tensor | None = None, v_scale: torch.Tensor | None = None,
-                           out: torch.Tensor | None = None, out_dtype: torch.dtype = torch.float32,
-                           workspace: torch.Tensor | None = None,
-                           table_offsets: torch.Tensor | None = None) -> torch.Tensor:
-    """Decode attention for q [num_seqs][Hq][D]; returns out [num_seqs][Hq][D]."""
+def _decode_operands(q, k_pool, v_pool, block_tables, context_lens, k_scale, v_scale, out, out_dtype,
+                     workspace, table_offsets):
     dev = _on_gpu(q, k_pool, v_pool, block_tables, context_lens, k_scale, v_scale, out, workspace, table_offsets)
     _check_pools(k_pool, v_pool, k_scale, v_scale)
     desc = cache_desc(k_pool)
@@ -233,9 +238,23 @@ def paged_attention_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.
     _contig(out, "out")
     maxb = max(block_tables.shape[1], 1)
     table_offsets = _offsets(table_offsets, b)
+    return dev, desc, b, hq, d, out, maxb, table_offsets
+
+
+def paged_attention_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                           block_tables: torch.Tensor, context_lens: torch.Tensor, softmax_scale: float,
+                           sliding_window: int = 0, partition_size: int = 512,
+                           k_scale: torch.Tensor | None = None, v_scale: torch.Tensor | None = None,
+                           out: torch.Tensor | None = None, out_dtype: torch.dtype = torch.float32,
+                           workspace: torch.Tensor | None = None,
+                           table_offsets: torch.Tensor | None = None) -> torch.Tensor:
+    """Decode attention for q [num_seqs][Hq][D]; returns out [num_seqs][Hq][D]."""
+    dev, desc, b, hq, d, out, maxb, table_offsets = _decode_operands(
+        q, k_pool, v_pool, block_tables, context_lens, k_scale, v_scale, out, out_dtype, workspace, table_offsets)
     need = decode_workspace_size(b, hq, d, maxb, desc.block_size, partition_size, table_offsets is not None) if b else 0
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        # zeroed: the work counter at its head must start at zero
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     lib = load_library()
     _check(lib.paged_attention_decode(
         ctypes.byref(desc), _ptr(q), _dtype(q, "q"), _ptr(out), _dtype(out, "out"), b, hq, _ptr(k_pool),

@@ -12,7 +12,10 @@
 //    counts in LDS; items 0 .. grid-1 go to the workgroups in order, later ones
 //    are claimed from a counter in the workspace (balanced, and the items in
 //    flight stay neighbours).  No host knowledge of the lengths is needed.  A
-//    batch whose every possible item has a workgroup needs no counter.
+//    batch whose every possible item has a workgroup needs no counter.  The
+//    counter clears itself: every workgroup stops at its first claim past the
+//    last item, so exactly `total` claims are made and the one that returns
+//    total - 1 is the last access of the launch; it stores 0 back.
 //  * Inside an item the 4 waves take the blocks round-robin.  Each wave streams
 //    its blocks' K and V tiles -- whole (block, KV head) runs, read with
 //    coalesced 16-byte loads -- as one sequence K0 V0 K1 V1 ..., each tile
@@ -49,7 +52,7 @@ struct DecodeArgs {
     void* out;
     float* part_ml;          // [num_seqs][Hq][max_parts][2]  running max (log2 units), sum
     float* part_o;           // [num_seqs][Hq][max_parts][D]  unnormalised outputs
-    unsigned* ticket;        // item counter (zero at launch), or null: items by stride
+    unsigned* ticket;        // item counter (zero at launch, zero again at exit), or null: items by stride
     const char* k_pool;
     const char* v_pool;
     const uint16_t* k_scale;
@@ -356,8 +359,17 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
     // the same blocks).  The item after the current one is known an item ahead
     // (s_next), so its loads can start before the current item is combined.
     const bool dyn = a.ticket != nullptr;
+    // one claim on the counter; the claim that returns total - 1 is the last one
+    // of the launch (each workgroup claims until it passes the last item, so
+    // claims 0 .. total - 1 are made), and it leaves the counter at zero for the
+    // next launch that uses this workspace
+    auto claim = [&]() {
+        const unsigned c = atomicAdd(a.ticket, 1u);
+        if (c == (unsigned)total - 1u) atomicExch(a.ticket, 0u);
+        return (int)c;
+    };
     if (dyn) {
-        if (tid == 0) s_next[1] = blockIdx.x < total ? (int)gridDim.x + (int)atomicAdd(a.ticket, 1u) : total;
+        if (tid == 0) s_next[1] = blockIdx.x < total ? (int)gridDim.x + claim() : total;
         __syncthreads();
     }
 
@@ -393,7 +405,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
     for (int item = blockIdx.x, following; item < total; item = following) {
         following = dyn ? __builtin_amdgcn_readfirstlane(s_next[parity ^ 1]) : item + (int)gridDim.x;
         int claimed = 0;
-        if (dyn && wave == 0 && lane == 0 && following < total) claimed = (int)atomicAdd(a.ticket, 1u);
+        if (dyn && wave == 0 && lane == 0 && following < total) claimed = claim();
         const bool have_next = following < total;
         const Item NI = item_info(have_next ? following : item);
         const int s = I.s, g = I.g, h0 = I.h0, nh = I.nh, k = I.kr, nparts = I.nparts;
@@ -683,10 +695,14 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
 }
 
 // Merge the partitions of every (sequence, head) with more than one:
-// out = sum_k 2^(m_k - M) o_k / sum_k 2^(m_k - M) l_k, M = max_k m_k.
-// One wave per (sequence, head): lane k owns partition k's weight (64 at a
-// time), broadcast with readlane; the D-wide partial rows are read 8
-// partitions at a time so their loads overlap.
+// out = sum_k 2^(m_k - M) o_k / sum_k 2^(m_k - M) l_k, M = max_k m_k; a
+// partition without keys (m_k = -inf) has weight 0, and a row with no key in
+// any partition is zero.  One wave per (sequence, head): lane k owns partition
+// k's weight (64 at a time), broadcast with readlane; the D-wide partial rows
+// are read kMergeBatch partitions at a time, all loads of a batch issued
+// before the first is used (most rows need one batch, so one round trip).
+constexpr int kMergeBatch = 32;
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecodeArgs a) {
     constexpr int E = D / kWave;                 // output elements per lane
@@ -711,28 +727,24 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecodeArgs a) {
         const int k = kb + lane;
         float w = 0.0f;
         if (k < n) {
-            w = fast_exp2(ml[2 * k] - M);
+            const float mk = ml[2 * k];
+            w = (mk == -INFINITY) ? 0.0f : fast_exp2(mk - M);
             den += w * ml[2 * k + 1];
         }
         const int cnt = min(kWave, n - kb);
-        int j = 0;
-        for (; j + 8 <= cnt; j += 8) {
-            float v[8][E];
+        for (int j = 0; j < cnt; j += kMergeBatch) {
+            float v[kMergeBatch][E];
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
+            for (int u = 0; u < kMergeBatch; ++u)
 #pragma unroll
-                for (int e = 0; e < E; ++e) v[u][e] = po[(int64_t)(kb + j + u) * D + e];
+                for (int e = 0; e < E; ++e) v[u][e] = (j + u < cnt) ? po[(int64_t)(kb + j + u) * D + e] : 0.0f;
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j + u));
+            for (int u = 0; u < kMergeBatch; ++u) {
+                const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w),
+                                                                                      (j + u) & (kWave - 1)));
 #pragma unroll
                 for (int e = 0; e < E; ++e) o[e] = fmaf(wu, v[u][e], o[e]);
             }
-        }
-        for (; j < cnt; ++j) {
-            const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j));
-#pragma unroll
-            for (int e = 0; e < E; ++e) o[e] = fmaf(wu, po[(int64_t)(kb + j) * D + e], o[e]);
         }
     }
     den = group_sum<kWave>(den);
@@ -744,12 +756,6 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecodeArgs a) {
         if (a.out_bf16) static_cast<uint16_t*>(a.out)[oi] = f32_to_bf16(r);
         else static_cast<float*>(a.out)[oi] = r;
     }
-}
-
-// Zero the item counter of the next partition launch (a kernel rather than a
-// memset, so the call can be captured in a graph).
-__global__ void decode_reset_kernel(unsigned* ticket) {
-    if (threadIdx.x == 0) *ticket = 0u;
 }
 
 // ---------------------------------------------------------------- host side
@@ -860,10 +866,6 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
         b.ticket = claim ? ticket : nullptr;
         const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(resident, (int64_t)n * per_seq_items));
         hipError_t e = hipSuccess;
-        if (claim) {
-            e = launch(decode_reset_kernel, dim3(1), dim3(kWave), 0, stream, ticket);
-            if (e != hipSuccess) return e;
-        }
         if (L.start_event) {
             e = hipEventRecord(L.start_event, stream);
             if (e != hipSuccess) return e;

@@ -235,13 +235,14 @@ size_t paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_q_hea
     return pkv::decode_workspace_bytes(num_seqs, num_q_heads, head_dim, np);
 }
 
-int paged_attention_decode(const pkv_cache_desc* cache, const void* q, int32_t q_dtype, void* out,
-                           int32_t out_dtype, int32_t num_seqs, int32_t num_q_heads, const void* k_pool,
-                           const void* v_pool, const void* k_scale, const void* v_scale,
-                           const int32_t* block_tables, int32_t max_blocks_per_seq,
-                           const int32_t* table_offsets, const int32_t* context_lens, float softmax_scale,
-                           int32_t sliding_window, int32_t partition_size, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+// Body of the decode entry point.
+static int decode_call(const pkv_cache_desc* cache, const void* q, int32_t q_dtype, void* out,
+                       int32_t out_dtype, int32_t num_seqs, int32_t num_q_heads, const void* k_pool,
+                       const void* v_pool, const void* k_scale, const void* v_scale,
+                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                       const int32_t* table_offsets, const int32_t* context_lens, float softmax_scale,
+                       int32_t sliding_window, int32_t partition_size, void* workspace,
+                       size_t workspace_bytes, void* stream) {
     g_error.clear();
     int rc = check_cache(cache);
     if (rc != PKV_OK) return rc;
@@ -272,14 +273,23 @@ int paged_attention_decode(const pkv_cache_desc* cache, const void* q, int32_t q
     const size_t need = paged_attention_decode_workspace_size(num_seqs, num_q_heads, cache->head_dim,
                                                               max_blocks_per_seq, cache->block_size, partition_size,
                                                               table_offsets != nullptr);
+    hipStream_t st = static_cast<hipStream_t>(stream);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(PKV_EWORKSPACE, "workspace of %zu bytes needed (got %zu)", need, workspace ? workspace_bytes : (size_t)0);
     if (need > 0 && !aligned(workspace, 256)) return fail(PKV_EINVAL, "workspace must be 256-byte aligned");
-    hipStream_t st = static_cast<hipStream_t>(stream);
     if (validate_env()) {
         rc = validate_tables(cache, num_seqs, block_tables, max_blocks_per_seq, table_offsets, context_lens,
                              nullptr, sliding_window, st);
         if (rc != PKV_OK) return rc;
+        if (need > 0) {
+            // the work counter at the head of the workspace must be zero
+            std::vector<uint32_t> head;
+            rc = copy_to_host(head, static_cast<const uint32_t*>(workspace), 1, st);
+            if (rc != PKV_OK) return rc;
+            if (head[0] != 0)
+                return fail(PKV_EINVAL, "workspace work counter is %u, expected 0 (zero the workspace before its "
+                            "first use)", head[0]);
+        }
     }
     pkv::DecodeLaunch L;
     L.q = q;
@@ -310,6 +320,18 @@ int paged_attention_decode(const pkv_cache_desc* cache, const void* q, int32_t q
     L.start_event = g_start_event;
     const hipError_t e = pkv::launch_decode(L, st);
     return e == hipSuccess ? PKV_OK : hip_fail(e, "paged_attention_decode launch");
+}
+
+int paged_attention_decode(const pkv_cache_desc* cache, const void* q, int32_t q_dtype, void* out,
+                           int32_t out_dtype, int32_t num_seqs, int32_t num_q_heads, const void* k_pool,
+                           const void* v_pool, const void* k_scale, const void* v_scale,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* table_offsets, const int32_t* context_lens, float softmax_scale,
+                           int32_t sliding_window, int32_t partition_size, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    return decode_call(cache, q, q_dtype, out, out_dtype, num_seqs, num_q_heads, k_pool, v_pool, k_scale, v_scale,
+                       block_tables, max_blocks_per_seq, table_offsets, context_lens, softmax_scale, sliding_window,
+                       partition_size, workspace, workspace_bytes, stream);
 }
 
 int paged_attention_prefill_chunk(const pkv_cache_desc* cache, const void* q, int32_t q_dtype, void* out,

@@ -2,7 +2,7 @@
 
 Chunks of new tokens are written through kv_cache_write into a NaN-poisoned,
 block-shuffled pool, then attended with causal and sliding-window masks on
-bf16 MFMA; sizes span several 128-row and 64-key tiles with ragged tails."""
+bf16 MFMA; sizes span several 256-row and 64-key tiles with ragged tails."""
 import numpy as np
 import pytest
 import torch
@@ -89,26 +89,50 @@ def test_prefill_single_row_chunks_match_decode_semantics():
     assert_close(out, expected_outputs(case), "bf16")
 
 
-def test_prefill_window_4096_full_size_sampled_rows():
+def _every_wave_rows(case):
+    """Chunk tokens that put a checked row in every wave of every row tile of
+    every (sequence, KV head) at the benchmark's launch shape (256 rows of
+    (token, query head) per workgroup, 32 per wave, so 8 tokens per wave with
+    G = 4): token 8w + (w % 8) of wave w, at a different lane each time."""
+    rows_per_wave = 32 // case.group
+    return [w * rows_per_wave + (w % rows_per_wave) for w in range(-(-int(case.new_lens.max()) // rows_per_wave))]
+
+
+def _check_rows_by_prefix_decode(case, out, kind):
+    """Each chosen chunk row against the oracle's decode over its prefix (pinned
+    equal to chunk rows), all rows of a sequence in one oracle call."""
+    picks = list(range(case.num_seqs))
+    toks = _every_wave_rows(case)
+    cache = build_cache(case, device=device())
+    q = to_numpy(case.q(device()))
+    cu = case.cu_q_lens
+    worst = 0.0
+    for s in picks:
+        L, C = int(case.seq_lens[s]), int(case.new_lens[s])
+        ii = [i for i in toks if i < C]
+        rows = np.array([cu[s] + i for i in ii])
+        lens = np.array([L - C + i + 1 for i in ii], np.int32)
+        # each row's table starts at the block of its first visible key (offset
+        # rows), so the oracle gathers its window rather than the whole context
+        offs = np.array([max(0, int(n) - case.window) // 16 if case.window > 0 else 0 for n in lens], np.int32)
+        tables = np.stack([np.concatenate([case.block_tables[s, o:], np.full(o, -1, np.int32)]) for o in offs])
+        ref = oracle.decode(cache, q[rows], "bf16", lens, tables, case.softmax_scale, case.window,
+                            table_offsets=offs)
+        worst = max(worst, assert_close(out[torch.from_numpy(rows).to(out.device)], ref, "bf16",
+                                        f"{kind} seq {s}"))
+    return worst
+
+
+def test_prefill_window_4096_full_size_every_wave():
     """16 sequences x 256 new tokens on 1024..16384-token contexts, window 4096,
-    32 q / 8 kv heads -- the benchmark's launch configuration.  Rows are
-    sampled (first/last of each 128-row tile edge) and checked against the
-    oracle's decode over the matching prefix (pinned equal to chunk rows)."""
+    32 q / 8 kv heads -- the benchmark's launch configuration.  One row in every
+    (sequence, KV head, row tile, wave) is checked against the oracle (all 32
+    query heads of 32 tokens per sequence)."""
     case = workloads.prefill_window()
     out, _ = _gpu(case)
     assert torch.isfinite(out).all()
-    picks = [int(np.argmin(case.seq_lens)), int(np.argmax(case.seq_lens)), 3]
-    sub = case.subset(sorted(set(picks)))
-    cache = build_cache(sub, device=device())
-    q = to_numpy(sub.q(device()))
-    cu_full = case.cu_q_lens
-    for si, s in enumerate(sorted(set(picks))):
-        L, C = int(case.seq_lens[s]), int(case.new_lens[s])
-        for i in (0, 1, 31, 32, 63, 127, 128, 200, 255):
-            row = int(sub.cu_q_lens[si]) + i
-            ref = oracle.decode(cache, q[row:row + 1], "bf16", np.array([L - C + i + 1], np.int32),
-                                sub.block_tables[si:si + 1], sub.softmax_scale, sub.window)
-            assert_close(out[cu_full[s] + i:cu_full[s] + i + 1], ref, "bf16", f"seq {s} row {i}")
+    err = _check_rows_by_prefix_decode(case, out, "bf16")
+    print(f"window-4096 prefill: {len(_every_wave_rows(case))} tokens per sequence checked, max abs error {err:.3e}")
 
 
 def test_prefill_zero_scale_and_empty_chunks():
@@ -158,26 +182,16 @@ def test_int8_prefill_zero_scale_empty_chunks_and_bf16_output():
     assert (np.abs(got - ref) <= bf16_ulp(ref) + 2e-3).all()
 
 
-def test_int8_prefill_window_4096_full_size_sampled_rows():
+def test_int8_prefill_window_4096_full_size_every_wave():
     """The window-4096 launch (16 x 256 rows on 1024..16384-token contexts,
-    32 q / 8 kv heads) over an INT8 pool; sampled rows against the oracle's
-    decode over the matching prefix of the dequantised cache."""
+    32 q / 8 kv heads) over an INT8 pool; one row in every (sequence, KV head,
+    row tile, wave) against the oracle's decode over the matching prefix of the
+    dequantised cache."""
     import dataclasses
     case = dataclasses.replace(workloads.prefill_window(), kv_dtype="i8", outliers=0.01)
     out, _ = _gpu(case)
     assert torch.isfinite(out).all()
-    picks = sorted({int(np.argmin(case.seq_lens)), int(np.argmax(case.seq_lens)), 6})
-    sub = case.subset(picks)
-    cache = build_cache(sub, device=device())
-    q = to_numpy(sub.q(device()))
-    cu_full = case.cu_q_lens
-    for si, s in enumerate(picks):
-        L, C = int(case.seq_lens[s]), int(case.new_lens[s])
-        for i in (0, 31, 64, 127, 128, 255):
-            row = int(sub.cu_q_lens[si]) + i
-            ref = oracle.decode(cache, q[row:row + 1], "bf16", np.array([L - C + i + 1], np.int32),
-                                sub.block_tables[si:si + 1], sub.softmax_scale, sub.window)
-            assert_close(out[cu_full[s] + i:cu_full[s] + i + 1], ref, "bf16", f"int8 seq {s} row {i}")
+    _check_rows_by_prefix_decode(case, out, "int8")
 
 
 # ---------------------------------------------------------------- mixed batches

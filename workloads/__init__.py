@@ -454,3 +454,88 @@ WORKLOADS = {
     "prefill-window": prefill_window,
     "mixed-step": mixed_step,
 }
+
+
+# ---------------------------------------------------------------- explicit and planted inputs
+class ExplicitCase(PagedCase):
+    """A PagedCase whose K, V and Q values are given as tensors instead of being
+    generated from the seed: ``K``, ``V`` are fp32 [num_counter_tokens][Hkv][D]
+    indexed by global token counter (tok_base[s] + p) and ``Q`` is fp32
+    [total_q][Hq][D]; each is rounded to ``in_dtype`` when handed out.  Tables,
+    lengths and pool come from the wrapped case."""
+
+    K: torch.Tensor = None
+    V: torch.Tensor = None
+    Q: torch.Tensor = None
+
+    @classmethod
+    def wrap(cls, case: PagedCase, K: torch.Tensor, V: torch.Tensor, Q: torch.Tensor) -> "ExplicitCase":
+        fields = {f: getattr(case, f) for f in case.__dataclass_fields__}
+        out = cls(**fields)
+        out.K, out.V, out.Q = K.float().contiguous(), V.float().contiguous(), Q.float().contiguous()
+        return out
+
+    def _pick(self, which):
+        return self.K if which == "k" else self.V
+
+    def kv(self, which, s, p0, p1, device="cpu"):
+        t0 = int(self.tok_base[s]) + p0
+        return self._convert(self._pick(which)[t0:t0 + max(p1 - p0, 0)].clone()).to(device)
+
+    def kv_tokens(self, which, t0, t1, device="cpu"):
+        return self._convert(self._pick(which)[t0:t1].clone()).to(device)
+
+    def kv_at(self, which, tokens, device="cpu"):
+        idx = torch.as_tensor(np.asarray(tokens, dtype=np.int64))
+        return self._convert(self._pick(which)[idx].clone()).to(device)
+
+    def q_rows(self, r0, r1, device="cpu"):
+        return self._convert(self.Q[r0:r1].clone()).to(device)
+
+    def subset(self, seqs) -> "ExplicitCase":
+        return ExplicitCase.wrap(super().subset(seqs), self.K, self.V, self.Q)
+
+
+def rising_scores(case: PagedCase, jump_log2: float = 12.0, stair: int = 128, c: float = 4.0,
+                  period: int = 0, seed_tag: int = TAG_MISC) -> ExplicitCase:
+    """Inputs whose attention scores rise along the context in steps.
+
+    For every (sequence, KV head) a unit direction u is drawn.  Each query row
+    of that head group becomes its generated value with the component along u
+    replaced by c * u, and each key at position j becomes its generated value
+    with the component along u replaced by r_j * u, where
+        r_j = jump_log2 * n_j / (c * softmax_scale * log2(e)),
+        n_j = floor(j / stair)  (or floor(j / stair) mod period, period > 0).
+    So every query of the group sees scores (in log2 units, softmax scale and
+    log2 e applied) equal to its random part plus jump_log2 * n_j: each step
+    of keys outscores everything before it (in its period) by jump_log2, and
+    an online softmax that meets the steps in order must rescale what it has
+    accumulated.  A period keeps the scores' range bounded over long contexts
+    (fp32 rounding of a score grows with its size).  V keeps its generated
+    values.  The result is an ExplicitCase with the same tables, lengths and
+    pool."""
+    hkv, hq, d = case.num_kv_heads, case.num_q_heads, case.head_dim
+    G = hq // hkv
+    ntok = int(case.tok_base[-1] + case.seq_lens[-1]) if case.num_seqs else 0
+    K = normal_f32(case.seed, TAG_K, 0, ntok * hkv * d).view(ntok, hkv, d)
+    V = normal_f32(case.seed, TAG_V, 0, ntok * hkv * d).view(ntok, hkv, d)
+    Q = normal_f32(case.seed, TAG_Q, 0, case.total_q * hq * d).view(case.total_q, hq, d)
+    K, Q = K.double(), Q.double()
+    dirs = normal_f32(case.seed, seed_tag, 0, case.num_seqs * hkv * d).view(case.num_seqs, hkv, d).double()
+    dirs = dirs / dirs.norm(dim=-1, keepdim=True)
+    unit = float(case.softmax_scale) * math.log2(math.e)
+    for s in range(case.num_seqs):
+        L = int(case.seq_lens[s])
+        t0 = int(case.tok_base[s])
+        r0, r1 = int(case.q_base[s]), int(case.q_base[s]) + int(case.new_lens[s])
+        steps = torch.div(torch.arange(L, dtype=torch.float64), stair, rounding_mode="floor")
+        if period > 0:
+            steps = torch.remainder(steps, period)
+        r = jump_log2 * steps / (c * unit)
+        for g in range(hkv):
+            u = dirs[s, g]
+            ks = K[t0:t0 + L, g]
+            K[t0:t0 + L, g] = ks - (ks @ u)[:, None] * u[None, :] + r[:, None] * u[None, :]
+            qs = Q[r0:r1, g * G:(g + 1) * G]
+            Q[r0:r1, g * G:(g + 1) * G] = qs - (qs @ u)[..., None] * u + c * u
+    return ExplicitCase.wrap(case, K.float(), V, Q.float())
