@@ -183,6 +183,38 @@ int paged_attention_decode(const pkv_cache_desc* cache,
                            void* stream);
 
 /*
+ * paged_attention_decode_noalloc -- paged_attention_decode for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same arguments and results as
+ * paged_attention_decode (same kernels), without the workspace: the split-K
+ * partial results and the work counter live in a fixed device array of the
+ * library, of paged_attention_decode_noalloc_max_scratch() bytes (32 MiB),
+ * one copy on each GPU it runs on, held until the process ends.  Nothing is
+ * allocated or freed by the call.  A call whose workspace size
+ * (paged_attention_decode_workspace_size) exceeds that maximum is rejected
+ * with PKV_EWORKSPACE before anything is enqueued.  The first call on a GPU
+ * looks the array up there and clears its work counter with a kernel on
+ * `stream`; every call leaves the counter at zero.  All calls on one GPU
+ * share the array: calls that overlap in time on one GPU (other streams,
+ * other threads) race and give wrong results; serialise them.
+ */
+int paged_attention_decode_noalloc(const pkv_cache_desc* cache,
+                                   const void* q, int32_t q_dtype,
+                                   void* out, int32_t out_dtype,
+                                   int32_t num_seqs, int32_t num_q_heads,
+                                   const void* k_pool, const void* v_pool,
+                                   const void* k_scale, const void* v_scale,
+                                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                   const int32_t* table_offsets,
+                                   const int32_t* context_lens,
+                                   float softmax_scale, int32_t sliding_window,
+                                   int32_t partition_size,
+                                   void* stream);
+
+/* Bytes of the fixed scratch paged_attention_decode_noalloc uses on each GPU. */
+size_t paged_attention_decode_noalloc_max_scratch(void);
+
+/*
  * paged_attention_prefill_chunk -- a chunk of new query tokens per sequence.
  * ("PyTorch LLM Serving Engine", What is implemented: chunked prefill sharing
  * the step with decode work; Loading: write, then attend over the block table.)

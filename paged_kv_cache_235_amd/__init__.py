@@ -17,9 +17,10 @@ The library is loaded on first use; there is no CPU fallback.
 """
 from ._binding import (EXPORTS, LIB_PATH, BlockAllocator, CacheDesc, PagedKVError, build_slot_mapping,
                        cache_desc, decode_workspace, decode_workspace_size, kv_cache_copy_blocks, kv_cache_write, last_error,
-                       load_library, paged_attention_decode, paged_attention_prefill_chunk,
+                       load_library, paged_attention_decode, paged_attention_decode_noalloc,
+                       decode_noalloc_max_scratch, paged_attention_prefill_chunk,
                        set_decode_split_event, set_decode_start_event, version)
 
 __all__ = ["EXPORTS", "LIB_PATH", "BlockAllocator", "CacheDesc", "build_slot_mapping", "kv_cache_copy_blocks", "PagedKVError", "cache_desc", "decode_workspace", "decode_workspace_size",
-           "kv_cache_write", "last_error", "load_library", "paged_attention_decode",
+           "kv_cache_write", "last_error", "load_library", "paged_attention_decode", "paged_attention_decode_noalloc", "decode_noalloc_max_scratch",
            "paged_attention_prefill_chunk", "set_decode_split_event", "set_decode_start_event", "version"]

@@ -28,7 +28,8 @@ EXPORTS = ("kv_cache_write", "paged_attention_decode_workspace_size", "paged_att
            "pkv_build_slot_mapping", "kv_cache_copy_blocks", "pkv_allocator_create", "pkv_allocator_destroy",
            "pkv_allocator_num_free", "pkv_allocator_refcount", "pkv_allocator_alloc", "pkv_allocator_retain",
            "pkv_allocator_release", "pkv_seq_append", "pkv_seq_fork", "pkv_seq_truncate",
-           "pkv_seq_evict_window", "pkv_seq_compact")
+           "pkv_seq_evict_window", "pkv_seq_compact", "paged_attention_decode_noalloc",
+           "paged_attention_decode_noalloc_max_scratch")
 
 
 class PagedKVError(RuntimeError):
@@ -65,6 +66,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.paged_attention_decode.restype = ctypes.c_int
             lib.paged_attention_decode.argtypes = [D, P, i32, P, i32, i32, i32, P, P, P, P, P, i32, P, P,
                                                    f32, i32, i32, P, ctypes.c_size_t, P]
+            lib.paged_attention_decode_noalloc.restype = ctypes.c_int
+            lib.paged_attention_decode_noalloc.argtypes = [D, P, i32, P, i32, i32, i32, P, P, P, P, P, i32, P, P,
+                                                           f32, i32, i32, P]
+            lib.paged_attention_decode_noalloc_max_scratch.restype = ctypes.c_size_t
+            lib.paged_attention_decode_noalloc_max_scratch.argtypes = []
             lib.paged_attention_prefill_chunk.restype = ctypes.c_int
             lib.paged_attention_prefill_chunk.argtypes = [D, P, i32, P, i32, P, i32, i32, i32, P, P, P, P, P,
                                                           i32, P, P, f32, i32, P]
@@ -262,6 +268,31 @@ def paged_attention_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.
         float(softmax_scale), int(sliding_window), int(partition_size), _ptr(workspace) if need else None,
         need, _stream(dev)))
     return out
+
+
+def paged_attention_decode_noalloc(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                                   block_tables: torch.Tensor, context_lens: torch.Tensor, softmax_scale: float,
+                                   sliding_window: int = 0, partition_size: int = 512,
+                                   k_scale: torch.Tensor | None = None, v_scale: torch.Tensor | None = None,
+                                   out: torch.Tensor = None,
+                                   table_offsets: torch.Tensor | None = None) -> torch.Tensor:
+    """paged_attention_decode with the library's fixed scratch instead of a
+    workspace: the caller passes ``out`` and the library allocates nothing."""
+    if out is None:
+        raise ValueError("paged_attention_decode_noalloc writes into a caller-provided out")
+    dev, desc, b, hq, d, out, maxb, table_offsets = _decode_operands(
+        q, k_pool, v_pool, block_tables, context_lens, k_scale, v_scale, out, out.dtype, None, table_offsets)
+    lib = load_library()
+    _check(lib.paged_attention_decode_noalloc(
+        ctypes.byref(desc), _ptr(q), _dtype(q, "q"), _ptr(out), _dtype(out, "out"), b, hq, _ptr(k_pool),
+        _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), maxb, _ptr(table_offsets), _ptr(context_lens),
+        float(softmax_scale), int(sliding_window), int(partition_size), _stream(dev)))
+    return out
+
+
+def decode_noalloc_max_scratch() -> int:
+    """Bytes of the fixed scratch the allocation-free decode uses on each GPU."""
+    return int(load_library().paged_attention_decode_noalloc_max_scratch())
 
 
 def paged_attention_prefill_chunk(q: torch.Tensor, cu_q_lens: torch.Tensor, seq_lens: torch.Tensor,

@@ -33,6 +33,8 @@
 //    poisoned (NaN) tail slots cannot leak.
 //  * With more than one partition per sequence the items write unnormalised
 //    partial results (m, l, o) and a second kernel merges them (log-sum-exp).
+#include <mutex>
+
 #include "pkv_internal.h"
 #include "pkv_device.h"
 
@@ -756,6 +758,46 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecodeArgs a) {
         if (a.out_bf16) static_cast<uint16_t*>(a.out)[oi] = f32_to_bf16(r);
         else static_cast<float*>(a.out)[oi] = r;
     }
+}
+
+// ------------------------------------------------- fixed scratch (no allocation)
+// Scratch of paged_attention_decode_noalloc: a file-scope device array, one
+// copy per GPU, held until the process ends.  In host code `scratch` names a
+// host-side stand-in, not device memory: kernels get the address that
+// hipGetSymbolAddress returns for the current device, looked up once per
+// device at the first call there.  Its first 256 bytes are the work counter,
+// which every call leaves at zero.
+constexpr size_t kFixedScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kFixedScratchBytes];
+
+__global__ void decode_clear_counter_kernel(unsigned* counter) {
+    if (threadIdx.x == 0) *counter = 0u;
+}
+
+size_t decode_fixed_scratch_bytes() { return kFixedScratchBytes; }
+
+hipError_t decode_fixed_scratch(void** ptr, hipStream_t stream) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        // set-up on this device: the counter starts at zero (a kernel, so a
+        // first call made under graph capture records no memset)
+        e = launch(decode_clear_counter_kernel, dim3(1), dim3(kWave), 0, stream, static_cast<unsigned*>(p));
+        if (e != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
 }
 
 // ---------------------------------------------------------------- host side

@@ -235,14 +235,15 @@ size_t paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_q_hea
     return pkv::decode_workspace_bytes(num_seqs, num_q_heads, head_dim, np);
 }
 
-// Body of the decode entry point.
+// Shared body of the two decode entry points.  fixed_scratch: the workspace is
+// the library's fixed device array (looked up here), not the caller's.
 static int decode_call(const pkv_cache_desc* cache, const void* q, int32_t q_dtype, void* out,
                        int32_t out_dtype, int32_t num_seqs, int32_t num_q_heads, const void* k_pool,
                        const void* v_pool, const void* k_scale, const void* v_scale,
                        const int32_t* block_tables, int32_t max_blocks_per_seq,
                        const int32_t* table_offsets, const int32_t* context_lens, float softmax_scale,
                        int32_t sliding_window, int32_t partition_size, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+                       size_t workspace_bytes, bool fixed_scratch, void* stream) {
     g_error.clear();
     int rc = check_cache(cache);
     if (rc != PKV_OK) return rc;
@@ -274,6 +275,15 @@ static int decode_call(const pkv_cache_desc* cache, const void* q, int32_t q_dty
                                                               max_blocks_per_seq, cache->block_size, partition_size,
                                                               table_offsets != nullptr);
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (fixed_scratch && need > 0) {
+        workspace_bytes = pkv::decode_fixed_scratch_bytes();
+        if (need > workspace_bytes)
+            return fail(PKV_EWORKSPACE, "this call needs %zu bytes of split-K scratch; the fixed scratch of "
+                        "paged_attention_decode_noalloc holds %zu (use a larger partition_size, fewer sequences, "
+                        "or paged_attention_decode with a workspace)", need, workspace_bytes);
+        const hipError_t e = pkv::decode_fixed_scratch(&workspace, st);
+        if (e != hipSuccess) return hip_fail(e, "fixed decode scratch");
+    }
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(PKV_EWORKSPACE, "workspace of %zu bytes needed (got %zu)", need, workspace ? workspace_bytes : (size_t)0);
     if (need > 0 && !aligned(workspace, 256)) return fail(PKV_EINVAL, "workspace must be 256-byte aligned");
@@ -331,8 +341,22 @@ int paged_attention_decode(const pkv_cache_desc* cache, const void* q, int32_t q
                            size_t workspace_bytes, void* stream) {
     return decode_call(cache, q, q_dtype, out, out_dtype, num_seqs, num_q_heads, k_pool, v_pool, k_scale, v_scale,
                        block_tables, max_blocks_per_seq, table_offsets, context_lens, softmax_scale, sliding_window,
-                       partition_size, workspace, workspace_bytes, stream);
+                       partition_size, workspace, workspace_bytes, false, stream);
 }
+
+int paged_attention_decode_noalloc(const pkv_cache_desc* cache, const void* q, int32_t q_dtype, void* out,
+                                   int32_t out_dtype, int32_t num_seqs, int32_t num_q_heads, const void* k_pool,
+                                   const void* v_pool, const void* k_scale, const void* v_scale,
+                                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                   const int32_t* table_offsets, const int32_t* context_lens,
+                                   float softmax_scale, int32_t sliding_window, int32_t partition_size,
+                                   void* stream) {
+    return decode_call(cache, q, q_dtype, out, out_dtype, num_seqs, num_q_heads, k_pool, v_pool, k_scale, v_scale,
+                       block_tables, max_blocks_per_seq, table_offsets, context_lens, softmax_scale, sliding_window,
+                       partition_size, nullptr, 0, true, stream);
+}
+
+size_t paged_attention_decode_noalloc_max_scratch(void) { return pkv::decode_fixed_scratch_bytes(); }
 
 int paged_attention_prefill_chunk(const pkv_cache_desc* cache, const void* q, int32_t q_dtype, void* out,
                                   int32_t out_dtype, const int32_t* cu_q_lens, int32_t num_seqs,

@@ -72,6 +72,11 @@ int32_t decode_max_partitions(int32_t max_blocks_per_seq, int32_t block_size, in
 size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                               int32_t max_partitions);
 hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream);
+// The fixed device scratch of the allocation-free decode entry point: its size,
+// and its address on the current device (looked up, and its work counter
+// cleared by a kernel on `stream`, at the first call on each device).
+size_t decode_fixed_scratch_bytes();
+hipError_t decode_fixed_scratch(void** ptr, hipStream_t stream);
 
 struct PrefillLaunch {
     const void* q;             // bf16 [rows][Hq][D]
