@@ -701,9 +701,11 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
 // partition without keys (m_k = -inf) has weight 0, and a row with no key in
 // any partition is zero.  One wave per (sequence, head): lane k owns partition
 // k's weight (64 at a time), broadcast with readlane; the D-wide partial rows
-// are read kMergeBatch partitions at a time, all loads of a batch issued
-// before the first is used (most rows need one batch, so one round trip).
-constexpr int kMergeBatch = 32;
+// are read kMergeBatch partitions at a time.  The first batch's loads do not
+// depend on the weights, so they are issued together with the loads of the
+// maxima: a row of up to kMergeBatch partitions (most rows) waits for memory
+// once.
+constexpr int kMergeBatch = 8;
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecodeArgs a) {
@@ -718,8 +720,21 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecodeArgs a) {
     const float* ml = a.part_ml + (int64_t)pair * a.max_parts * 2;
     const float* po = a.part_o + (int64_t)pair * a.max_parts * D + lane * E;
 
-    float M = -INFINITY;
-    for (int k = lane; k < n; k += kWave) M = fmaxf(M, ml[2 * k]);
+    float v[kMergeBatch][E];
+    auto load_batch = [&](int k0) {
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u)
+#pragma unroll
+            for (int e = 0; e < E; ++e) v[u][e] = (k0 + u < n) ? po[(int64_t)(k0 + u) * D + e] : 0.0f;
+    };
+    load_batch(0);
+    float mk0 = -INFINITY, lk0 = 0.0f;           // this lane's partition of the first 64
+    if (lane < n) {
+        mk0 = ml[2 * lane];
+        lk0 = ml[2 * lane + 1];
+    }
+    float M = mk0;
+    for (int k = lane + kWave; k < n; k += kWave) M = fmaxf(M, ml[2 * k]);
     M = group_max<kWave>(M);
     float den = 0.0f;
     float o[E];
@@ -729,17 +744,14 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecodeArgs a) {
         const int k = kb + lane;
         float w = 0.0f;
         if (k < n) {
-            const float mk = ml[2 * k];
+            const float mk = kb == 0 ? mk0 : ml[2 * k];
+            const float lk = kb == 0 ? lk0 : ml[2 * k + 1];
             w = (mk == -INFINITY) ? 0.0f : fast_exp2(mk - M);
-            den += w * ml[2 * k + 1];
+            den += w * lk;
         }
         const int cnt = min(kWave, n - kb);
         for (int j = 0; j < cnt; j += kMergeBatch) {
-            float v[kMergeBatch][E];
-#pragma unroll
-            for (int u = 0; u < kMergeBatch; ++u)
-#pragma unroll
-                for (int e = 0; e < E; ++e) v[u][e] = (j + u < cnt) ? po[(int64_t)(kb + j + u) * D + e] : 0.0f;
+            if (kb + j > 0) load_batch(kb + j);
 #pragma unroll
             for (int u = 0; u < kMergeBatch; ++u) {
                 const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w),

@@ -560,6 +560,401 @@ __global__ __launch_bounds__(64 * W) void prefill_pipe_kernel(PrefillArgs a) {
         }
 }
 
+// ---------------------------------------------------------------- bf16 pools, head_dim 128
+// The same work decomposition, online softmax and MFMA layouts as
+// prefill_pipe_kernel, with the K tiles copied from the pool straight into LDS
+// (no registers, no VALU, no LDS store instructions) and one barrier per tile:
+//  * K: each wave copies 8 of a tile's 64 rows, one 256-byte row per
+//    global_load_lds_dword (lane l's 4 bytes land at the row's LDS address +
+//    4 l), so each row keeps its 16-byte pad and the MFMA operand reads stay
+//    conflict-free.  LDS row R holds key swap23(R); rows 8w .. 8w+7 of wave w
+//    all lie in block w / 2 of the tile.
+//  * V: staged through registers as before (converted to fp16 and transposed).
+//  * Two K slots and two V slots.  Iteration t: store V(t+1) (loaded during
+//    iteration t-1) into its slot, start copying K(t+2) and loading V(t+2),
+//    then the softmax of tile t with tile t+1's S^T MFMAs, then P.V of tile t;
+//    then wait for this wave's loads and copies and pass the one barrier.
+//    Each slot is overwritten only after the barrier that follows its last
+//    reader.
+// The copies are issued with inline asm (the compiler would otherwise wait for
+// every outstanding load before each LDS read, which defeats the prefetch);
+// the waits for them are explicit, and M0 is saved and restored around each.
+
+// Eight 256-byte K rows of one (block, KV head) run, at keys {0, 1, 2, 3, 8, 9,
+// 10, 11} from `src`, to eight consecutive padded LDS rows (272 bytes apart)
+// from LDS address `lds`: lane l's 4 bytes of each row from row + 4 l to the
+// LDS row + 4 l.  A global_load_lds writes LDS address M0 + offset + 4 lane,
+// where the instruction's immediate offset moves the global address too, so
+// the offsets stay 0: the rows' global offsets come in `voff` (lane l: 4 l +
+// 256 k for keys k = 0..3, keys 8..11 from a second base 2048 bytes on), and
+// M0 steps by one padded row.  One asm block: M0 is saved and restored,
+// `s_nop 4` first (a VMEM read of an SGPR that a VALU op has just written
+// needs 5 wait states), `s_nop 0` after each M0 write (an LDS copy reading M0
+// right after a SALU write of it needs 1).
+__device__ __forceinline__ void lds_copy_k8(uint32_t lds, const uint16_t* src, const uint32_t (&voff)[4]) {
+    const uint32_t m = __builtin_amdgcn_readfirstlane(lds);
+    const uint64_t gp = (uint64_t)(uintptr_t)src;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)gp);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(gp >> 32));
+    const uint64_t g0 = ((uint64_t)hi << 32) | lo;
+    const uint64_t g1 = g0 + 2048;
+    uint32_t saved;
+    asm volatile(
+        "s_nop 4\n\t"
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %2, %6\n\t"
+        "s_add_u32 m0, m0, 0x110\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %3, %6\n\t"
+        "s_add_u32 m0, m0, 0x110\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %4, %6\n\t"
+        "s_add_u32 m0, m0, 0x110\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %5, %6\n\t"
+        "s_add_u32 m0, m0, 0x110\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %2, %7\n\t"
+        "s_add_u32 m0, m0, 0x110\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %3, %7\n\t"
+        "s_add_u32 m0, m0, 0x110\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %4, %7\n\t"
+        "s_add_u32 m0, m0, 0x110\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %5, %7\n\t"
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0"
+        : "=&s"(saved)
+        : "s"(m), "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(g0), "s"(g1)
+        : "memory", "scc");
+}
+
+// Wait for every load and LDS copy this wave has issued, and for its LDS
+// stores, then the workgroup barrier.
+__device__ __forceinline__ void wait_all_and_barrier() {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <bool ZS>
+__global__ __launch_bounds__(512) void prefill_ring_kernel(PrefillArgs a) {
+    constexpr int D = 128;
+    constexpr int NTH = 512;                    // 8 waves
+    constexpr int ROWS = 256;                   // query rows per workgroup
+    constexpr int KS = D + 8;                   // halfwords per K row in LDS (272 bytes)
+    constexpr int DK = D / 16;                  // k-steps of Q.K^T
+    constexpr int NT = D / 32;                  // 32-wide d tiles of the output
+    constexpr float kRescale = 8.0f;            // rescale O only when a row max grows by > 2^8
+    __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kKeys * KS];
+    __shared__ __attribute__((aligned(16))) uint16_t s_vt[2][D * kVtStride];   // V^T as fp16
+
+    // ---- work item (as in prefill_pipe_kernel)
+    const int units = a.total / a.m_tiles;
+    const int xcd = blockIdx.x % kXcds;
+    const int j = blockIdx.x / kXcds;
+    const int unit = (j / a.m_tiles) * kXcds + xcd;
+    if (unit >= units) return;
+    const int mt = j % a.m_tiles;
+    const int w_idx = unit * a.m_tiles + mt;
+    const int g = (w_idx / a.m_tiles) % a.num_kv_heads;
+    const int s = w_idx / (a.m_tiles * a.num_kv_heads);
+    const int G = a.group;
+    const int q0 = a.cu_q_lens[s];
+    const int C = a.cu_q_lens[s + 1] - q0;
+    const int off = a.table_offsets ? max(0, a.table_offsets[s]) : 0;
+    const int L = (int)min((int64_t)a.seq_lens[s], ((int64_t)a.max_blocks + off) * kBlk);
+    const int nrows = C * G;
+    const int r0 = mt * ROWS;
+    if (r0 >= nrows || C <= 0 || C > L) return;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = lane >> 5;
+    const int base_pos = L - C;
+    const int p_min = base_pos + r0 / G;
+    const int p_max = base_pos + (min(nrows, r0 + ROWS) - 1) / G;
+
+    const int row = r0 + wave * 32 + (lane & 31);
+    const bool row_ok = row < nrows;
+    const int tok = row_ok ? row / G : 0;
+    const int jh = row_ok ? row - tok * G : 0;
+    const int p_row = row_ok ? base_pos + tok : p_max;
+    bf16x8_t qf[DK];
+    {
+        const uint16_t* qp = a.q + ((int64_t)(q0 + tok) * a.num_q_heads + g * G + jh) * D + 8 * h;
+#pragma unroll
+        for (int ks = 0; ks < DK; ++ks) {
+            u32x4_t v = {0u, 0u, 0u, 0u};
+            if (row_ok) v = *reinterpret_cast<const u32x4_t*>(qp + 16 * ks);
+            qf[ks] = as_bf16x8(v);
+        }
+    }
+
+    f32x16_t o[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[nt][v] = 0.0f;
+    float m_used = -INFINITY;
+    float l_run = 0.0f;
+
+    const int k_lo = (a.window > 0) ? max(0, p_min - a.window + 1) : 0;
+    const int kt_first = max((k_lo / kKeys) * kKeys, off * kBlk);
+    const int n_tiles = kt_first <= p_max ? (p_max - kt_first) / kKeys + 1 : 0;
+    const int last_blk = (L - 1) / kBlk;
+    const __attribute__((address_space(4))) int32_t* table =
+        (const __attribute__((address_space(4))) int32_t*)(a.block_tables + (int64_t)s * a.max_blocks - off);
+    const int64_t head_stride = (int64_t)kBlk * D;
+    const int64_t blk_stride = (int64_t)a.num_kv_heads * head_stride;
+    const uint16_t* k_pool = static_cast<const uint16_t*>(a.k_pool);
+    const uint16_t* v_pool = static_cast<const uint16_t*>(a.v_pool);
+
+    auto kt_of = [&](int t) { return kt_first + kKeys * t; };
+    // physical block of block b of the tile at kt (block 0 when the entry is not a
+    // block of the pool: those keys are masked), and the tile's validity mask
+    auto block_id = [&](int kt, int b, bool& ok) {
+        const int lb = kt / kBlk + b;
+        const int id = lb <= last_blk ? table[lb] : -1;
+        ok = id >= 0 && id < a.num_blocks;
+        return ok ? id : 0;
+    };
+    auto tile_mask = [&](int kt) {
+        int m = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            bool ok;
+            (void)block_id(kt, b, ok);
+            m |= (ok ? 1 : 0) << b;
+        }
+        return m;
+    };
+
+    // ---- this wave's K rows: R = 8 wave + i, in block wave / 2 of the tile, row R
+    // holding key swap23(R) = 4 (wave & 1) + {0, 1, 2, 3, 8, 9, 10, 11}[i]
+    const int my_blk = wave >> 1;
+    const int key0 = (wave & 1) * 4;
+    const uint32_t k_lds[2] = {
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)&s_k[0][8 * wave * KS],
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)&s_k[1][8 * wave * KS]};
+    static_assert(KS * 2 == 0x110 && D * 2 == 256, "row strides assumed by lds_copy_k8");
+    const uint32_t k_voff[4] = {(uint32_t)lane * 4u, (uint32_t)lane * 4u + 256u, (uint32_t)lane * 4u + 512u,
+                                (uint32_t)lane * 4u + 768u};
+    auto copy_k = [&](int slot, int kt) {
+        bool ok;
+        const int id = block_id(kt, my_blk, ok);
+        const uint16_t* src = k_pool + (int64_t)id * blk_stride + g * head_stride + key0 * D;
+        lds_copy_k8(slot ? k_lds[1] : k_lds[0], src, k_voff);
+    };
+
+    // ---- V: thread tid stages dims 2 v_dp, +1 of keys 8 v_kg .. +8 (block v_kg / 2 = wave / 2)
+    const int v_dp = tid % (D / 2);
+    const int v_kg = wave;
+    const int v_off = ((8 * v_kg) % kBlk) * D + 2 * v_dp;
+    uint32_t vreg[8];
+    auto load_v = [&](int kt) {
+        bool ok;
+        const int id = block_id(kt, v_kg / 2, ok);
+        const uint16_t* vp = v_pool + (int64_t)id * blk_stride + g * head_stride + v_off;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) vreg[i] = *reinterpret_cast<const uint32_t*>(vp + i * D);
+    };
+    auto store_v = [&](int slot, int kt, int m) {
+        uint32_t w[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w[i] = vreg[i];
+        if (m != 15 || kt + kKeys > L) {        // edge tile (uniform branch): zero dead keys, they may hold NaN
+            const bool blk_live = (m >> (v_kg / 2)) & 1;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) w[i] = (blk_live && kt + 8 * v_kg + i < L) ? w[i] : 0u;
+        }
+        // 8 keys x 2 dims -> 2 rows of 8 keys, bf16 -> fp16
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            u32x4_t r;
+#pragma unroll
+            for (int mm = 0; mm < 4; ++mm)
+                r[mm] = e ? pack_f16x2(bf16hi(w[2 * mm]), bf16hi(w[2 * mm + 1]))
+                          : pack_f16x2(bf16lo(w[2 * mm]), bf16lo(w[2 * mm + 1]));
+            const int d = 2 * v_dp + e;
+            *reinterpret_cast<u32x4_t*>(&s_vt[slot][d * kVtStride + vt_col(d, v_kg)]) = r;
+        }
+    };
+
+    // S^T of a staged tile for the wave's 32 rows (as in prefill_pipe_kernel)
+    auto compute_s = [&](f32x16_t* S, int slot) {
+#pragma unroll
+        for (int T = 0; T < 2; ++T)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) S[T][v] = 0.0f;
+        const uint16_t* kr0 = &s_k[slot][(lane & 31) * KS + 8 * h];
+        const uint16_t* kr1 = kr0 + 32 * KS;
+        u32x4_t k0 = *reinterpret_cast<const u32x4_t*>(kr0);
+        u32x4_t k1 = *reinterpret_cast<const u32x4_t*>(kr1);
+#pragma unroll
+        for (int ks = 0; ks < DK; ++ks) {
+            u32x4_t n0 = k0, n1 = k1;
+            if (ks + 1 < DK) {
+                n0 = *reinterpret_cast<const u32x4_t*>(kr0 + 16 * (ks + 1));
+                n1 = *reinterpret_cast<const u32x4_t*>(kr1 + 16 * (ks + 1));
+            }
+            S[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k0), qf[ks], S[0], 0, 0, 0);
+            S[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k1), qf[ks], S[1], 0, 0, 0);
+            k0 = n0;
+            k1 = n1;
+        }
+    };
+
+    // masks, online softmax and O^T += V^T P^T for tile t (scores in S, V in slot);
+    // the next tile's S^T MFMAs (from K slot slot ^ 1) go out in the same basic
+    // block as the exp2 work.  On the last tile that slot holds stale data: the
+    // MFMAs read in-bounds LDS and the result is never used.
+    const float sl2 = a.scale_log2;
+    auto finish_tile = [&](f32x16_t* S, f32x16_t* S_nxt, int slot, int kt, int tmask) {
+        const bool full = tmask == 15 && kt + kKeys - 1 <= p_min && (a.window <= 0 || kt >= p_max - a.window + 1);
+        if (!full) {
+#pragma unroll
+            for (int T = 0; T < 2; ++T)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int key = kt + 32 * T + 16 * (v / 8) + 8 * h + (v % 8);
+                    const bool vis = ((tmask >> ((key - kt) / kBlk)) & 1) && key <= p_row &&
+                                     (a.window <= 0 || key > p_row - a.window);
+                    S[T][v] = vis ? S[T][v] : -INFINITY;
+                }
+        }
+        float mt_ = -INFINITY;
+#pragma unroll
+        for (int T = 0; T < 2; ++T)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) mt_ = fmaxf(mt_, S[T][v]);
+        mt_ = fmaxf(mt_, __shfl_xor(mt_, 32, kWave));
+        const float m_tile = mt_ == -INFINITY ? -INFINITY : mt_ * sl2;
+        const bool grow = m_tile > m_used + kRescale || (m_used == -INFINITY && m_tile != -INFINITY);
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+            const float m_new = grow ? m_tile : m_used;
+            const float alpha = (m_used == -INFINITY) ? 0.0f : fast_exp2(m_used - m_new);
+            m_used = m_new;
+            const float f = grow ? alpha : 1.0f;
+            l_run *= f;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) o[nt][v] *= f;
+        }
+        const float msub = (m_used == -INFINITY) ? 0.0f : m_used;
+        compute_s(S_nxt, slot ^ 1);
+        const uint16_t* vt_base = &s_vt[slot][(lane & 31) * kVtStride + 8 * (h ^ ((lane >> 4) & 1))];
+        uint32_t pw[2][8];                       // P^T as fp16 pairs: [T][4u + word]
+        if constexpr (!ZS) {
+#pragma unroll
+            for (int T = 0; T < 2; ++T)
+#pragma unroll
+                for (int v = 0; v < 16; v += 2)
+                    pw[T][v / 2] = pack_f16x2(fast_exp2(fmaf(S[T][v], sl2, -msub)),
+                                              fast_exp2(fmaf(S[T][v + 1], sl2, -msub)));
+        } else {
+#pragma unroll
+            for (int T = 0; T < 2; ++T)
+#pragma unroll
+                for (int v = 0; v < 16; v += 2) {
+                    const float x0 = S[T][v], x1 = S[T][v + 1];
+                    const float p0 = (x0 == -INFINITY) ? 0.0f : fast_exp2(fmaf(x0, sl2, -msub));
+                    const float p1 = (x1 == -INFINITY) ? 0.0f : fast_exp2(fmaf(x1, sl2, -msub));
+                    pw[T][v / 2] = pack_f16x2(p0, p1);
+                }
+        }
+        {
+            const f16x2_t one = {(_Float16)1.0f, (_Float16)1.0f};
+            float ls0 = 0.0f, ls1 = 0.0f;
+#pragma unroll
+            for (int w = 0; w < 8; ++w) {
+                ls0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pw[0][w]), one, ls0, false);
+                ls1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pw[1][w]), one, ls1, false);
+            }
+            l_run += ls0 + ls1;
+        }
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int T = ks >> 1, u = ks & 1;
+            u32x4_t pb;
+            pb[0] = pw[T][4 * u + 0]; pb[1] = pw[T][4 * u + 1];
+            pb[2] = pw[T][4 * u + 2]; pb[3] = pw[T][4 * u + 3];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const int vo = 32 * nt * kVtStride + 16 * ((ks ^ nt) & 7);
+                const u32x4_t vv = *reinterpret_cast<const u32x4_t*>(vt_base + vo);
+                o[nt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(vv), as_f16x8(pb), o[nt], 0, 0, 0);
+            }
+        }
+    };
+
+    // ---- prologue: K(0), K(1) copied, V(0) staged, S^T(0), V(1) in registers
+    int mk0 = 0, mk1 = 0;                       // validity masks of tiles t and t + 1
+    f32x16_t sa[2], sb[2];
+    if (n_tiles > 0) {
+        mk0 = tile_mask(kt_of(0));
+        copy_k(0, kt_of(0));
+        load_v(kt_of(0));
+    }
+    if (n_tiles > 1) {
+        mk1 = tile_mask(kt_of(1));
+        copy_k(1, kt_of(1));
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (n_tiles > 0) store_v(0, kt_of(0), mk0);
+    if (n_tiles > 1) load_v(kt_of(1));
+    wait_all_and_barrier();                     // K(0), K(1), V(0) in LDS
+    // unconditional, so Q's first use is on every path into the loop
+    compute_s(sa, 0);
+    wait_all_and_barrier();                     // every wave is done reading K slot 0
+
+    auto step = [&](f32x16_t* s_cur, f32x16_t* s_nxt, int t) {
+        const int slot = t & 1;
+        if (t + 1 < n_tiles) store_v(slot ^ 1, kt_of(t + 1), mk1);
+        int mk2 = 0;
+        if (t + 2 < n_tiles) {
+            mk2 = tile_mask(kt_of(t + 2));
+            copy_k(slot, kt_of(t + 2));
+            load_v(kt_of(t + 2));
+        }
+        finish_tile(s_cur, s_nxt, slot, kt_of(t), mk0);
+        wait_all_and_barrier();
+        mk0 = mk1;
+        mk1 = mk2;
+    };
+    for (int t = 0; t < n_tiles; t += 2) {
+        step(sa, sb, t);
+        if (t + 1 < n_tiles) step(sb, sa, t + 1);
+    }
+
+    // ---- normalise and store
+    const float l_row = l_run + __shfl_xor(l_run, 32, kWave);
+    if (!row_ok) return;
+    const float inv = l_row > 0.0f ? 1.0f / l_row : 0.0f;
+    const int64_t obase = ((int64_t)(q0 + tok) * a.num_q_heads + g * G + jh) * D;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+            const int d = 32 * nt + 8 * v4 + 4 * h;
+            const float r0_ = o[nt][4 * v4 + 0] * inv, r1_ = o[nt][4 * v4 + 1] * inv;
+            const float r2_ = o[nt][4 * v4 + 2] * inv, r3_ = o[nt][4 * v4 + 3] * inv;
+            if (a.out_bf16) {
+                u32x2_t pk;
+                pk[0] = pack_bf16x2(r0_, r1_);
+                pk[1] = pack_bf16x2(r2_, r3_);
+                *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(a.out) + obase + d) = pk;
+            } else {
+                f32x4_t fv = {r0_, r1_, r2_, r3_};
+                *reinterpret_cast<f32x4_t*>(static_cast<float*>(a.out) + obase + d) = fv;
+            }
+        }
+}
+
 }  // namespace
 
 hipError_t launch_prefill(const PrefillLaunch& L, hipStream_t stream) {
@@ -604,8 +999,8 @@ hipError_t launch_prefill(const PrefillLaunch& L, hipStream_t stream) {
     if (L.head_dim == 64)
         return zs ? launch(prefill_pipe_kernel<64, kPipeWaves, true, false>, g3, b3, 0, stream, a)
                   : launch(prefill_pipe_kernel<64, kPipeWaves, false, false>, g3, b3, 0, stream, a);
-    return zs ? launch(prefill_pipe_kernel<128, kPipeWaves, true, false>, g3, b3, 0, stream, a)
-              : launch(prefill_pipe_kernel<128, kPipeWaves, false, false>, g3, b3, 0, stream, a);
+    return zs ? launch(prefill_ring_kernel<true>, g3, b3, 0, stream, a)
+              : launch(prefill_ring_kernel<false>, g3, b3, 0, stream, a);
 }
 
 }  // namespace pkv
