@@ -42,12 +42,19 @@ def build() -> str:
 
 
 def lib() -> ctypes.CDLL:
+    """The compiled oracle (built on first use).  The environment variable
+    PKV_ORACLE_LIBRARY names another build of the same source to load instead
+    (the sanitizer run of the CPU tests uses one)."""
     global _lib
     with _lock:
         if _lib is None:
-            if not os.path.exists(LIB_PATH) or os.path.getmtime(LIB_PATH) < os.path.getmtime(SOURCE):
-                build()
-            _lib = _declare(ctypes.CDLL(LIB_PATH))
+            other = os.environ.get("PKV_ORACLE_LIBRARY")
+            if other:
+                _lib = _declare(ctypes.CDLL(other))
+            else:
+                if not os.path.exists(LIB_PATH) or os.path.getmtime(LIB_PATH) < os.path.getmtime(SOURCE):
+                    build()
+                _lib = _declare(ctypes.CDLL(LIB_PATH))
     return _lib
 
 

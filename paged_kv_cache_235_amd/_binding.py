@@ -48,9 +48,12 @@ _lock = threading.Lock()
 _lib = None
 
 
-def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libpagedkv (once).  Raises if it has not been built."""
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load libpagedkv (once).  Raises if it has not been built.  The
+    environment variable PKV_LIBRARY names another build of the same library
+    (the sanitizer run of the CPU tests uses one)."""
     global _lib
+    path = path or os.environ.get("PKV_LIBRARY") or LIB_PATH
     with _lock:
         if _lib is None:
             if not os.path.exists(path):

@@ -63,6 +63,10 @@ constexpr int kKeys = 64;               // keys per tile
 constexpr int kBlk = 16;
 constexpr int kVtStride = kKeys + 8;    // halfwords per V^T row (16-byte aligned)
 constexpr int kXcds = 8;
+#ifndef PKV_RING_WAVES
+#define PKV_RING_WAVES 8
+#endif
+constexpr int kRingWaves = PKV_RING_WAVES;  // waves per workgroup of the bf16 head_dim-128 kernel
 
 struct PrefillArgs {
     const uint16_t* q;
@@ -639,11 +643,18 @@ __device__ __forceinline__ void wait_all_and_barrier() {
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <bool ZS>
-__global__ __launch_bounds__(512) void prefill_ring_kernel(PrefillArgs a) {
+// W waves per workgroup (4 or 8), two waves per SIMD either way: with W = 4
+// two workgroups share a CU, so the two waves of a SIMD belong to different
+// workgroups and do not meet at the same barriers.
+template <int W, bool ZS>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_ring_kernel(PrefillArgs a) {
     constexpr int D = 128;
-    constexpr int NTH = 512;                    // 8 waves
-    constexpr int ROWS = 256;                   // query rows per workgroup
+    constexpr int NTH = 64 * W;
+    constexpr int ROWS = 32 * W;                // query rows per workgroup
+    constexpr int KROWS = kKeys / W;            // K rows of a tile each wave copies (8 or 16)
+    constexpr int NVP = 8 * (D / 2) / NTH;      // V pieces each thread stages (1 or 2)
+    static_assert(KROWS % 8 == 0 && NVP >= 1, "staging shape");
     constexpr int KS = D + 8;                   // halfwords per K row in LDS (272 bytes)
     constexpr int DK = D / 16;                  // k-steps of Q.K^T
     constexpr int NT = D / 32;                  // 32-wide d tiles of the output
@@ -733,54 +744,63 @@ __global__ __launch_bounds__(512) void prefill_ring_kernel(PrefillArgs a) {
         return m;
     };
 
-    // ---- this wave's K rows: R = 8 wave + i, in block wave / 2 of the tile, row R
-    // holding key swap23(R) = 4 (wave & 1) + {0, 1, 2, 3, 8, 9, 10, 11}[i]
-    const int my_blk = wave >> 1;
-    const int key0 = (wave & 1) * 4;
-    const uint32_t k_lds[2] = {
-        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)&s_k[0][8 * wave * KS],
-        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)&s_k[1][8 * wave * KS]};
+    // ---- this wave's K rows: groups of 8 rows R0 + i (R0 = KROWS wave + 8 c), in
+    // block R0 / 16 of the tile, row R holding key swap23(R) = key0 + {0, 1, 2,
+    // 3, 8, 9, 10, 11}[i] of that block, key0 = 4 when R0 is 8 past a block start
     static_assert(KS * 2 == 0x110 && D * 2 == 256, "row strides assumed by lds_copy_k8");
     const uint32_t k_voff[4] = {(uint32_t)lane * 4u, (uint32_t)lane * 4u + 256u, (uint32_t)lane * 4u + 512u,
                                 (uint32_t)lane * 4u + 768u};
     auto copy_k = [&](int slot, int kt) {
-        bool ok;
-        const int id = block_id(kt, my_blk, ok);
-        const uint16_t* src = k_pool + (int64_t)id * blk_stride + g * head_stride + key0 * D;
-        lds_copy_k8(slot ? k_lds[1] : k_lds[0], src, k_voff);
+#pragma unroll
+        for (int c = 0; c < KROWS / 8; ++c) {
+            const int r0 = KROWS * wave + 8 * c;
+            bool ok;
+            const int id = block_id(kt, r0 / kBlk, ok);
+            const uint16_t* src = k_pool + (int64_t)id * blk_stride + g * head_stride + ((r0 / 8) & 1) * 4 * D;
+            lds_copy_k8((uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)&s_k[slot][r0 * KS], src,
+                        k_voff);
+        }
     };
 
-    // ---- V: thread tid stages dims 2 v_dp, +1 of keys 8 v_kg .. +8 (block v_kg / 2 = wave / 2)
+    // ---- V: piece (v_kg, v_dp) = dims 2 v_dp, +1 of keys 8 v_kg .. +8 (block
+    // v_kg / 2); thread tid stages pieces v_kg = wave + W n, v_dp = tid % 64
     const int v_dp = tid % (D / 2);
-    const int v_kg = wave;
-    const int v_off = ((8 * v_kg) % kBlk) * D + 2 * v_dp;
-    uint32_t vreg[8];
+    uint32_t vreg[NVP][8];
     auto load_v = [&](int kt) {
-        bool ok;
-        const int id = block_id(kt, v_kg / 2, ok);
-        const uint16_t* vp = v_pool + (int64_t)id * blk_stride + g * head_stride + v_off;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) vreg[i] = *reinterpret_cast<const uint32_t*>(vp + i * D);
+        for (int n = 0; n < NVP; ++n) {
+            const int v_kg = wave + W * n;
+            bool ok;
+            const int id = block_id(kt, v_kg / 2, ok);
+            const uint16_t* vp = v_pool + (int64_t)id * blk_stride + g * head_stride +
+                                 ((8 * v_kg) % kBlk) * D + 2 * v_dp;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) vreg[n][i] = *reinterpret_cast<const uint32_t*>(vp + i * D);
+        }
     };
     auto store_v = [&](int slot, int kt, int m) {
-        uint32_t w[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) w[i] = vreg[i];
-        if (m != 15 || kt + kKeys > L) {        // edge tile (uniform branch): zero dead keys, they may hold NaN
-            const bool blk_live = (m >> (v_kg / 2)) & 1;
+        for (int n = 0; n < NVP; ++n) {
+            const int v_kg = wave + W * n;
+            uint32_t w[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) w[i] = (blk_live && kt + 8 * v_kg + i < L) ? w[i] : 0u;
-        }
-        // 8 keys x 2 dims -> 2 rows of 8 keys, bf16 -> fp16
+            for (int i = 0; i < 8; ++i) w[i] = vreg[n][i];
+            if (m != 15 || kt + kKeys > L) {    // edge tile (uniform branch): zero dead keys, they may hold NaN
+                const bool blk_live = (m >> (v_kg / 2)) & 1;
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            u32x4_t r;
+                for (int i = 0; i < 8; ++i) w[i] = (blk_live && kt + 8 * v_kg + i < L) ? w[i] : 0u;
+            }
+            // 8 keys x 2 dims -> 2 rows of 8 keys, bf16 -> fp16
 #pragma unroll
-            for (int mm = 0; mm < 4; ++mm)
-                r[mm] = e ? pack_f16x2(bf16hi(w[2 * mm]), bf16hi(w[2 * mm + 1]))
-                          : pack_f16x2(bf16lo(w[2 * mm]), bf16lo(w[2 * mm + 1]));
-            const int d = 2 * v_dp + e;
-            *reinterpret_cast<u32x4_t*>(&s_vt[slot][d * kVtStride + vt_col(d, v_kg)]) = r;
+            for (int e = 0; e < 2; ++e) {
+                u32x4_t r;
+#pragma unroll
+                for (int mm = 0; mm < 4; ++mm)
+                    r[mm] = e ? pack_f16x2(bf16hi(w[2 * mm]), bf16hi(w[2 * mm + 1]))
+                              : pack_f16x2(bf16lo(w[2 * mm]), bf16lo(w[2 * mm + 1]));
+                const int d = 2 * v_dp + e;
+                *reinterpret_cast<u32x4_t*>(&s_vt[slot][d * kVtStride + vt_col(d, v_kg)]) = r;
+            }
         }
     };
 
@@ -999,8 +1019,15 @@ hipError_t launch_prefill(const PrefillLaunch& L, hipStream_t stream) {
     if (L.head_dim == 64)
         return zs ? launch(prefill_pipe_kernel<64, kPipeWaves, true, false>, g3, b3, 0, stream, a)
                   : launch(prefill_pipe_kernel<64, kPipeWaves, false, false>, g3, b3, 0, stream, a);
-    return zs ? launch(prefill_ring_kernel<true>, g3, b3, 0, stream, a)
-              : launch(prefill_ring_kernel<false>, g3, b3, 0, stream, a);
+    // bf16, head_dim 128: the ring kernel, kRingWaves waves (32 rows each) per workgroup
+    PrefillArgs r = a;
+    r.m_tiles = (int32_t)((rows + 32 * kRingWaves - 1) / (32 * kRingWaves));
+    const int64_t rtotal = (int64_t)L.num_seqs * L.num_kv_heads * r.m_tiles;
+    if (rtotal > INT32_MAX / 2) return hipErrorInvalidValue;
+    r.total = (int32_t)rtotal;
+    const dim3 rg((unsigned)(((units + kXcds - 1) / kXcds) * r.m_tiles * kXcds)), rb(64 * kRingWaves);
+    return zs ? launch(prefill_ring_kernel<kRingWaves, true>, rg, rb, 0, stream, r)
+              : launch(prefill_ring_kernel<kRingWaves, false>, rg, rb, 0, stream, r);
 }
 
 }  // namespace pkv
