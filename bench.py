@@ -403,7 +403,7 @@ def bench_prefill(args, torch, pkv, workloads, tl, kv_dtype="bf16"):
     fl = prefill_flops(case)
     sec = float(np.mean(t)) / 1e3
     tf = fl / sec / 1e12
-    kern = "prefill_pipe_kernel<D=128, 8 waves>" if kv_dtype == "bf16" else "prefill_pipe_kernel<D=128, 8 waves, INT8>"
+    kern = "prefill_ring_kernel<W=8> (bf16 pool, head_dim 128)" if kv_dtype == "bf16" else "prefill_pipe_kernel<D=128, 8 waves, INT8>"
     return {"workload": "chunked prefill: 16 sequences x 256 new tokens on 1024..16384-token paged "
                         f"contexts, 32 q / 8 kv heads, head_dim 128, {kv_dtype} pool, causal + window 4096",
             "us_per_call": round(sec * 1e6, 2), "us_p10": round(float(np.percentile(t, 10)) * 1e3, 2),
@@ -477,7 +477,8 @@ def bench_mixed(args, torch, pkv, workloads, tl):
     """A serving step mixing 16 prefill chunks (256 tokens each) with 240 decode
     rows, window 4096: one prefill-kernel launch over the whole batch, against
     two launches on the same pool (prefill kernel over the chunks, decode kernel
-    over the decode rows).  Sampled rows of both are checked against the oracle."""
+    over the decode rows), on one stream and on two streams that may overlap.
+    Sampled rows of each are checked against the oracle."""
     dev = torch.device("cuda", 0)
     case = workloads.mixed_step()
     pools = tl.alloc_pools(case, dev)
@@ -488,6 +489,7 @@ def bench_mixed(args, torch, pkv, workloads, tl):
     rows_pf = int(case.cu_q_lens[npf])
     out = torch.empty(q.shape, dtype=torch.float32, device=dev)
     out2 = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    out3 = torch.empty(q.shape, dtype=torch.float32, device=dev)
     workspace = pkv.decode_workspace(case.num_seqs - npf, case.num_q_heads, case.head_dim, case.max_blocks_per_seq,
                                      case.block_size, 512, device=dev)
     cu_pf = cu[:npf + 1].contiguous()
@@ -504,11 +506,32 @@ def bench_mixed(args, torch, pkv, workloads, tl):
                                    sliding_window=case.window, partition_size=512, out=out2[rows_pf:],
                                    workspace=workspace)
 
+    s_a, s_b = torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)    # default priority
+
+    def two_streams():
+        # the same two launches on two streams, free to run at the same time
+        cur = torch.cuda.current_stream(dev)
+        e0 = torch.cuda.Event()
+        e0.record(cur)
+        s_a.wait_event(e0)
+        s_b.wait_event(e0)
+        with torch.cuda.stream(s_b):
+            pkv.paged_attention_decode(q[rows_pf:], pools["k"], pools["v"], bt[npf:], lens[npf:], case.softmax_scale,
+                                       sliding_window=case.window, partition_size=512, out=out3[rows_pf:],
+                                       workspace=workspace)
+        with torch.cuda.stream(s_a):
+            pkv.paged_attention_prefill_chunk(q[:rows_pf], cu_pf, lens[:npf], pools["k"], pools["v"], bt[:npf],
+                                              case.max_q_len, case.softmax_scale, sliding_window=case.window,
+                                              out=out3[:rows_pf])
+        cur.wait_stream(s_a)
+        cur.wait_stream(s_b)
+
     res = {"workload": "mixed serving step: 16 prefill chunks of 256 tokens on 1024..16384-token contexts + "
                        "240 decode rows on clipped log-normal contexts (median 2048), 32 q / 8 kv heads, "
                        "head_dim 128, bf16, window 4096",
            "algorithmic_flops": prefill_flops(case)}
-    for name, fn in (("one_launch_prefill_kernel", one), ("two_launches_prefill_plus_decode", two)):
+    for name, fn in (("one_launch_prefill_kernel", one), ("two_launches_prefill_plus_decode", two),
+                     ("two_launches_on_two_streams", two_streams)):
         for _ in range(args.warmup):
             fn()
         torch.cuda.synchronize()
@@ -538,7 +561,9 @@ def bench_mixed(args, torch, pkv, workloads, tl):
                                 sub.block_tables[si:si + 1], sub.softmax_scale, sub.window)
             r = int(case.cu_q_lens[s_]) + i
             err = max(err, tl.assert_close(out[r:r + 1], ref, "bf16", "mixed one launch"),
-                      tl.assert_close(out2[r:r + 1], ref, "bf16", "mixed two launches"))
+                      tl.assert_close(out2[r:r + 1], ref, "bf16", "mixed two launches"),
+                      tl.assert_close(out3[r:r + 1], ref, "bf16", "mixed two streams"))
+    res["two_streams_equal_one_stream"] = bool(torch.equal(out2, out3))
     res["max_abs_err_sampled"] = float(err)
     del pools
     torch.cuda.empty_cache()
