@@ -139,9 +139,12 @@ size_t paged_attention_decode_workspace_size(int32_t num_seqs, int32_t num_q_hea
  *   out           [num_seqs][num_q_heads][head_dim] of out_dtype (F32 or BF16).
  *   k_scale/v_scale  INT8 pools only, else NULL.
  *   block_tables  [num_seqs][max_blocks_per_seq] int32 physical block ids;
- *                 entries past ceil(L / block_size) are never read, and with a
+ *                 entries past ceil(L / block_size) are never used, and with a
  *                 window neither are entries wholly before it (they may be -1
- *                 after pkv_seq_evict_window).
+ *                 after pkv_seq_evict_window).  Every entry of the array must
+ *                 be readable: a single-pass call (no partitions) with no
+ *                 window and no table_offsets reads a row's leading entries
+ *                 before it knows L, and ignores those past it.
  *   table_offsets NULL, or [num_seqs] int32 >= 0: column c of row s holds
  *                 logical block c + table_offsets[s], so a windowed sequence's
  *                 row can drop its released blocks (pkv_seq_compact) and stay

@@ -188,7 +188,9 @@ constexpr int tb_dup(int n, int bit) {
     return bit == 0 ? 0 : (n >= 2 ? tb_dup((n + 1) / 2, bit / 2) : (bit | tb_dup(1, bit / 2)));
 }
 
-template <int KV, int D, int GT>
+// DIRECT: a single-pass call (no partitions) with no window and no table
+// offsets; the host launches this variant only then.
+template <int KV, int D, int GT, bool DIRECT>
 __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a) {
     using C = Cfg<KV, D, GT>;
     constexpr int NT = tb_count(C::NV, C::LPR / 2);   // logits per lane after the butterfly
@@ -209,8 +211,15 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int B = a.num_seqs;
 
+    // Single-pass calls with no window and no table offsets (DIRECT): every
+    // sequence is one item per (KV head, head chunk) and its keys start at 0, so
+    // an item's sequence and first table columns are known from its index
+    // alone -- no prefix, and the context length and the table ids are read at
+    // the same time instead of one after the other.
+    constexpr bool direct = DIRECT;
+
     // ---- prefix of partition counts (each thread owns up to 8 consecutive sequences)
-    {
+    if constexpr (!direct) {
         const int per = (B + kThreads - 1) / kThreads;
         int cnt[8];
         int sum = 0;
@@ -248,7 +257,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
     }
 
     const int HC = a.num_kv_heads * a.head_chunks;
-    const int total = s_prefix[B] * HC;
+    const int total = direct ? B * HC : s_prefix[B] * HC;
     const int row_lane = lane / C::LPR;          // row of this lane inside each load
     const int col = (lane % C::LPR) * C::EPL;    // first column of this lane
 
@@ -264,16 +273,24 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
         const int hchunk = hc - I.g * a.head_chunks;
         // LDS values are the same in every lane: keep them in scalar registers
         auto uni = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
-        int lo_s = 0, hi_s = B - 1;                 // largest s with s_prefix[s] <= gp
-        while (lo_s < hi_s) {
-            const int mid = (lo_s + hi_s + 1) >> 1;
-            if (uni(s_prefix[mid]) <= gp) lo_s = mid; else hi_s = mid - 1;
+        int ps, L;
+        if constexpr (direct) {
+            I.s = gp;
+            ps = gp;
+            I.nparts = 1;
+            L = seq_len(a, I.s);
+        } else {
+            int lo_s = 0, hi_s = B - 1;             // largest s with s_prefix[s] <= gp
+            while (lo_s < hi_s) {
+                const int mid = (lo_s + hi_s + 1) >> 1;
+                if (uni(s_prefix[mid]) <= gp) lo_s = mid; else hi_s = mid - 1;
+            }
+            I.s = lo_s;
+            ps = uni(s_prefix[I.s]);
+            I.nparts = uni(s_prefix[I.s + 1]) - ps;
+            L = uni(s_len[I.s]);
         }
-        I.s = lo_s;
-        const int ps = uni(s_prefix[I.s]);
-        I.nparts = uni(s_prefix[I.s + 1]) - ps;
-        const int L = uni(s_len[I.s]);
-        const int lo = min(first_key(a, L, uni(seq_off(a, I.s))), L);
+        const int lo = direct ? 0 : min(first_key(a, L, uni(seq_off(a, I.s))), L);
         const int P = a.part_tokens;
         I.k = (P > 0 ? lo / P : 0) + (gp - ps);
         I.kr = gp - ps;
@@ -336,7 +353,13 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
         // column of the lane's block in the sequence's row (blocks before the row's
         // offset have been released: no id)
         const int col = c0 / kBlk + wave + kWaves * lane - I.off;
-        if (lane < nbw && col >= 0 && col < a.max_blocks) id = a.block_tables[(int64_t)I.s * a.max_blocks + col];
+        if constexpr (direct) {
+            // read before the wave's block count is known (it needs the context
+            // length); entries past the sequence are never used
+            if (col < a.max_blocks) id = a.block_tables[(int64_t)I.s * a.max_blocks + col];
+        } else if (lane < nbw && col >= 0 && col < a.max_blocks) {
+            id = a.block_tables[(int64_t)I.s * a.max_blocks + col];
+        }
         return id;
     };
     auto valid_id = [&](int id) { return id >= 0 && id < a.num_blocks; };
@@ -815,25 +838,30 @@ hipError_t decode_fixed_scratch(void** ptr, hipStream_t stream) {
 // ---------------------------------------------------------------- host side
 using PartKernel = void (*)(DecodeArgs);
 
-template <int KV, int D>
+template <int KV, int D, bool DIRECT>
 static PartKernel pick_gt(int gt) {
     switch (gt) {
-    case 1: return decode_partition_kernel<KV, D, 1>;
-    case 2: return decode_partition_kernel<KV, D, 2>;
-    case 3: return decode_partition_kernel<KV, D, 3>;
-    case 4: return decode_partition_kernel<KV, D, 4>;
-    case 5: return decode_partition_kernel<KV, D, 5>;
-    case 6: return decode_partition_kernel<KV, D, 6>;
-    case 7: return decode_partition_kernel<KV, D, 7>;
-    default: return decode_partition_kernel<KV, D, 8>;
+    case 1: return decode_partition_kernel<KV, D, 1, DIRECT>;
+    case 2: return decode_partition_kernel<KV, D, 2, DIRECT>;
+    case 3: return decode_partition_kernel<KV, D, 3, DIRECT>;
+    case 4: return decode_partition_kernel<KV, D, 4, DIRECT>;
+    case 5: return decode_partition_kernel<KV, D, 5, DIRECT>;
+    case 6: return decode_partition_kernel<KV, D, 6, DIRECT>;
+    case 7: return decode_partition_kernel<KV, D, 7, DIRECT>;
+    default: return decode_partition_kernel<KV, D, 8, DIRECT>;
     }
 }
 
-static PartKernel pick(KvKind kv, int D, int gt) {
-    if (kv == KV_F32) return D == 64 ? pick_gt<KV_F32, 64>(gt) : pick_gt<KV_F32, 128>(gt);
-    if (kv == KV_BF16) return D == 64 ? pick_gt<KV_BF16, 64>(gt) : pick_gt<KV_BF16, 128>(gt);
-    if (kv == KV_I8Q) return D == 64 ? pick_gt<KV_I8Q, 64>(gt) : pick_gt<KV_I8Q, 128>(gt);
-    return D == 64 ? pick_gt<KV_I8, 64>(gt) : pick_gt<KV_I8, 128>(gt);
+template <bool DIRECT>
+static PartKernel pick_kv(KvKind kv, int D, int gt) {
+    if (kv == KV_F32) return D == 64 ? pick_gt<KV_F32, 64, DIRECT>(gt) : pick_gt<KV_F32, 128, DIRECT>(gt);
+    if (kv == KV_BF16) return D == 64 ? pick_gt<KV_BF16, 64, DIRECT>(gt) : pick_gt<KV_BF16, 128, DIRECT>(gt);
+    if (kv == KV_I8Q) return D == 64 ? pick_gt<KV_I8Q, 64, DIRECT>(gt) : pick_gt<KV_I8Q, 128, DIRECT>(gt);
+    return D == 64 ? pick_gt<KV_I8, 64, DIRECT>(gt) : pick_gt<KV_I8, 128, DIRECT>(gt);
+}
+
+static PartKernel pick(KvKind kv, int D, int gt, bool direct) {
+    return direct ? pick_kv<true>(kv, D, gt) : pick_kv<false>(kv, D, gt);
 }
 
 int32_t decode_max_partitions(int32_t max_blocks_per_seq, int32_t block_size, int32_t partition_size,
@@ -883,7 +911,10 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
     a.q_bf16 = L.q_bf16;
     a.out_bf16 = L.out_bf16;
 
-    PartKernel kern = pick(L.kv, L.head_dim, gt);
+    // single pass, no window, no table offsets: the variant that maps items to
+    // sequences directly
+    const bool direct = !merge && L.window <= 0 && L.table_offsets == nullptr;
+    PartKernel kern = pick(L.kv, L.head_dim, gt, direct);
     static thread_local PartKernel occ_kern = nullptr;
     static thread_local int occ = 0;
     if (occ_kern != kern) {

@@ -20,7 +20,8 @@ happens after a wave's first tile, so these tests build inputs that force it:
   * a softmax scale of 1e4: the result must be finite and one-hot on the
     best key (the stability case);
   * V at the edges of the bf16 prefill path's fp16 range (|v| up to 60000,
-    and below 2^-14), and rows whose table entries hold no block.
+    and below 2^-14), an INT8-pool decode query far outside binary16's range,
+    and rows whose table entries hold no block.
 
 Tolerances are those of pkv_testlib (bf16: abs 2e-3 and per-vector relative
 1e-2; fp32: abs 1e-5), against the fp64 oracle on the same inputs.
@@ -222,6 +223,32 @@ def test_prefill_and_decode_with_v_below_fp16_normal_range():
     for part in (0, 512):
         out = _decode_gpu(dec, partition_size=part)
         assert_close(out / f, ref / f, "bf16", f"decode |v| < 2^-14 P={part}")
+
+
+# ---------------------------------------------------------------- INT8 pools: query magnitude
+@pytest.mark.parametrize("log2f", [18, 0, -30])
+def test_int8_decode_query_far_outside_fp16_range(log2f):
+    """INT8 pools with a bf16 query keep the query's full exponent range: Q
+    multiplied by 2^log2f (2^18: |q| past binary16's largest finite value;
+    2^-30: every |q| below its smallest normal) with the softmax scale divided
+    by the same factor, so the weights stay those of the unscaled case; the
+    usual tolerances apply."""
+    f = 2.0 ** log2f
+    base = workloads.make_case("i8qmag", 111, [1, 17, 600, 2100], [1] * 4, 8, 2, 128, kv_dtype="i8")
+    ntok = int(base.tok_base[-1] + base.seq_lens[-1])
+    hd = base.num_kv_heads * base.head_dim
+    K = workloads.normal_f32(base.seed, workloads.TAG_K, 0, ntok * hd).view(ntok, base.num_kv_heads, -1)
+    V = workloads.normal_f32(base.seed, workloads.TAG_V, 0, ntok * hd).view(ntok, base.num_kv_heads, -1)
+    Q = workloads.normal_f32(base.seed, workloads.TAG_Q, 0, base.total_q * base.num_q_heads * base.head_dim) * f
+    case = workloads.ExplicitCase.wrap(dataclasses.replace(base, softmax_scale=base.softmax_scale / f), K, V,
+                                       Q.view(base.total_q, base.num_q_heads, -1))
+    q = case.q()
+    assert (float(q.abs().max()) > 65504.0) if log2f > 0 else True
+    assert (float(q.abs().max()) < 2.0 ** -14) if log2f < 0 else True
+    ref = expected_outputs(case)
+    for part in (0, 512):
+        out = _decode_gpu(case, partition_size=part)
+        assert_close(out, ref, "bf16", f"q x 2^{log2f} P={part}")
 
 
 # ---------------------------------------------------------------- entries without a block
