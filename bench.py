@@ -608,7 +608,7 @@ def bench_decode_shapes(args, torch, pkv, workloads, tl):
         nbytes = sum(by.values())
         entry = {"workload": name, "context_tokens": int(case.seq_lens.sum()), "algorithmic_bytes": nbytes,
                  "by_partition_size": {}}
-        for part in (64, 128, 256, 512):
+        for part in (0, 64, 128, 256, 512):
             workspace = pkv.decode_workspace(case.num_seqs, case.num_q_heads, case.head_dim,
                                              case.max_blocks_per_seq, case.block_size, part, device=dev)
 

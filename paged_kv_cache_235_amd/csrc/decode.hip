@@ -275,10 +275,17 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
         auto uni = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
         int ps, L;
         if constexpr (direct) {
+            // one item per (sequence, KV head, head chunk), keys from 0 to L
             I.s = gp;
-            ps = gp;
-            I.nparts = 1;
             L = seq_len(a, I.s);
+            I.nparts = 1;
+            I.k = I.kr = 0;
+            I.off = 0;
+            I.t0 = 0;
+            I.t1 = L;
+            I.h0 = I.g * a.group + hchunk * GT;
+            I.nh = min(GT, a.group - hchunk * GT);
+            return I;
         } else {
             int lo_s = 0, hi_s = B - 1;             // largest s with s_prefix[s] <= gp
             while (lo_s < hi_s) {
@@ -290,7 +297,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
             I.nparts = uni(s_prefix[I.s + 1]) - ps;
             L = uni(s_len[I.s]);
         }
-        const int lo = direct ? 0 : min(first_key(a, L, uni(seq_off(a, I.s))), L);
+        const int lo = min(first_key(a, L, uni(seq_off(a, I.s))), L);
         const int P = a.part_tokens;
         I.k = (P > 0 ? lo / P : 0) + (gp - ps);
         I.kr = gp - ps;
