@@ -26,7 +26,8 @@
 //    butterfly and updates an online softmax: the running maximum only moves
 //    (with a rescale of what was accumulated) when a logit passes it by more
 //    than 2^8, which after the first tile is rare.  The probabilities go
-//    through LDS to the V step, which accumulates p * v.  At the end of the
+//    through LDS to the V step, which accumulates p * v (INT8 pools at
+//    head_dim 128: on the matrix cores, see the V step).  At the end of the
 //    item the 4 waves' (m, l, acc) are combined through LDS.
 //  * Keys outside the sequence, its window or a valid block are removed by
 //    selection (logit -inf, V row zeroed), never by multiplying by zero, so
@@ -39,6 +40,8 @@
 #include "pkv_device.h"
 
 namespace pkv {
+
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
@@ -434,6 +437,19 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
     }
     const bool owner = (lane & DUP) == 0;        // one lane per distinct quantity
 
+    // INT8 pools, head_dim 128: P.V on the matrix cores.  A lane's four loads of a
+    // tile hold keys 4t + q (t = 0..3, q = lane / 16) at its 8 columns, which is
+    // the B operand of v_mfma_f32_4x4x4bf16_1k (16 blocks of 4 lanes; lane 4b + r
+    // supplies row r of A and column r of B over k = t, and receives column r of
+    // D, rows t): B = the biased codes of one of the lane's columns (exact in
+    // bf16), A = the weights p * v_scale of head 4 nq + (lane & 3) at the same 4
+    // keys, as a bf16 value plus its bf16 remainder (two MFMAs, 16 bits of the
+    // weight), D = that column's partial output for 4 heads.  The keys of the
+    // other row groups are added in the combine, as for the FMA form.
+    constexpr bool MV = is_i8(KV) && D == 128;
+    constexpr int NHQ = (GT + 3) / 4;            // groups of 4 heads
+    const int hr = lane & 3;                     // this lane's head within a group
+
     for (int item = blockIdx.x, following; item < total; item = following) {
         following = dyn ? __builtin_amdgcn_readfirstlane(s_next[parity ^ 1]) : item + (int)gridDim.x;
         int claimed = 0;
@@ -445,12 +461,22 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
         // running softmax state of this wave's keys: m per head (uniform), the
         // same m per logit slot of this lane, l per logit slot, acc per column
         float m_run[GT], m_lane[NT], l_lane[NT], acc[GT][C::EPL], psum[GT];
+        f32x4_t accv[MV ? NHQ : 1][MV ? C::EPL : 1];  // MV: [head group][column] -> 4 heads
+        float psl[MV ? NHQ : 1];                     // MV: weight sum of head 4 nq + hr, this lane's keys
 #pragma unroll
         for (int j = 0; j < GT; ++j) {
             m_run[j] = -INFINITY;
             psum[j] = 0.0f;
 #pragma unroll
             for (int e = 0; e < C::EPL; ++e) acc[j][e] = 0.0f;
+        }
+        if constexpr (MV) {
+#pragma unroll
+            for (int nq = 0; nq < NHQ; ++nq) {
+                psl[nq] = 0.0f;
+#pragma unroll
+                for (int e = 0; e < C::EPL; ++e) accv[nq][e] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            }
         }
 #pragma unroll
         for (int kk = 0; kk < NT; ++kk) {
@@ -554,9 +580,15 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
                         const float m_new = fmaxf(m_run[j], group_max<kWave>(v));
                         const float alpha = (m_run[j] == -INFINITY) ? 0.0f : fast_exp2(m_run[j] - m_new);
                         m_run[j] = m_new;
-                        psum[j] *= alpha;
+                        if constexpr (MV) {
 #pragma unroll
-                        for (int e = 0; e < C::EPL; ++e) acc[j][e] *= alpha;
+                            for (int e = 0; e < C::EPL; ++e) accv[j >> 2][e][j & 3] *= alpha;
+                            psl[j >> 2] *= hr == (j & 3) ? alpha : 1.0f;
+                        } else {
+                            psum[j] *= alpha;
+#pragma unroll
+                            for (int e = 0; e < C::EPL; ++e) acc[j][e] *= alpha;
+                        }
 #pragma unroll
                         for (int kk = 0; kk < NT; ++kk)
                             if ((base + kk) % GT == j) {
@@ -583,6 +615,53 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
                 const int b = wave + kWaves * it;
                 const bool blk_ok = (okmask >> it) & 1;
                 const bool full = blk_ok && tbase + b * kBlk >= c0 && tbase + (b + 1) * kBlk <= c1;
+                if constexpr (MV) {
+                    // A: weights of head 4 nq + hr at keys 4t + q, hi and remainder
+                    bf16x4_t a_hi[NHQ], a_lo[NHQ];
+#pragma unroll
+                    for (int nq = 0; nq < NHQ; ++nq) {
+                        const int j = 4 * nq + hr;
+                        float w[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int r = i * C::RPL + row_lane;
+                            const int tok = tbase + b * kBlk + r;
+                            const bool row_ok = full || (blk_ok && tok >= c0 && tok < c1);
+                            const float pj = lp[r * C::GTP + (j < GT ? j : 0)];
+                            w[i] = (row_ok && j < GT) ? pj * t.sc[i] : 0.0f;
+                            psl[nq] += w[i];
+                        }
+                        const uint32_t h01 = pack_bf16x2(w[0], w[1]), h23 = pack_bf16x2(w[2], w[3]);
+                        const uint32_t l01 = pack_bf16x2(w[0] - bf16lo(h01), w[1] - bf16hi(h01));
+                        const uint32_t l23 = pack_bf16x2(w[2] - bf16lo(h23), w[3] - bf16hi(h23));
+                        a_hi[nq] = __builtin_bit_cast(bf16x4_t, u32x2_t{h01, h23});
+                        a_lo[nq] = __builtin_bit_cast(bf16x4_t, u32x2_t{l01, l23});
+                    }
+                    // B: column e's biased codes u = q8 + 128 at keys 4t + q, as bf16
+                    uint32_t u[4][2];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int wd = 0; wd < 2; ++wd) u[i][wd] = t.w[i].w[wd] ^ 0x80808080u;
+#pragma unroll
+                    for (int e = 0; e < C::EPL; ++e) {
+                        float f[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) f[i] = (float)((u[i][e >> 2] >> (8 * (e & 3))) & 0xffu);
+                        const uint32_t b01 = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, f[1]),
+                                                                   __builtin_bit_cast(uint32_t, f[0]), 0x07060302u);
+                        const uint32_t b23 = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, f[3]),
+                                                                   __builtin_bit_cast(uint32_t, f[2]), 0x07060302u);
+                        const bf16x4_t bv = __builtin_bit_cast(bf16x4_t, u32x2_t{b01, b23});
+#pragma unroll
+                        for (int nq = 0; nq < NHQ; ++nq)
+                            accv[nq][e] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(a_hi[nq], bv, accv[nq][e], 0, 0, 0);
+#pragma unroll
+                        for (int nq = 0; nq < NHQ; ++nq)
+                            accv[nq][e] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(a_lo[nq], bv, accv[nq][e], 0, 0, 0);
+                    }
+                    return;
+                }
 #pragma unroll
                 for (int i = 0; i < C::NLOAD; ++i) {
                     Words<C::WORDS> wv = t.w[i];
@@ -654,6 +733,16 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
             for (int kk = 0; kk < NT; ++kk)
                 if (kk < tb_valid && (tb_base + kk) % GT == j) v += l_lane[kk];
             l_run[j] = group_sum<kWave>(v);
+        }
+        if constexpr (MV) {
+            // heads' weight sums for this lane's keys: lane (lane & ~3) + (j & 3)
+            // holds head j's
+#pragma unroll
+            for (int j = 0; j < GT; ++j) psum[j] = __shfl(psl[j >> 2], (lane & ~3) | (j & 3), kWave);
+#pragma unroll
+            for (int j = 0; j < GT; ++j)
+#pragma unroll
+                for (int e = 0; e < C::EPL; ++e) acc[j][e] = accv[j >> 2][e][j & 3];
         }
         if constexpr (is_i8(KV)) {
 #pragma unroll
