@@ -184,6 +184,46 @@ __device__ __forceinline__ void load_tile(Tile<KV, D, GT>& t, const char* pool, 
     }
 }
 
+// An INT8 K tile (head_dim 128) laid out for Q.K^T on 4x4x4 MFMAs: load i
+// holds keys 4i .. 4i+3, lane l the 8 codes of key 4i + (l & 3) at columns
+// 8 (l >> 2) .. +7 (each load still reads one contiguous 512-byte run), so the
+// four lanes of an MFMA block hold four keys at the same columns; sc[0] is the
+// scale of key l >> 2, the key whose logit the lane ends up with.
+template <int KV, int D, int GT>
+__device__ __forceinline__ void load_tile_keys_by_lane(Tile<KV, D, GT>& t, const char* pool,
+                                                       const uint16_t* scales, int64_t tile, int lane) {
+    using C = Cfg<KV, D, GT>;
+    const char* p = pool + tile * C::TILE_BYTES + (lane & 3) * C::ROW_BYTES + (lane >> 2) * 8;
+#pragma unroll
+    for (int i = 0; i < C::NLOAD; ++i) t.w[i] = load_words<C::WORDS>(p + i * 4 * C::ROW_BYTES);
+    t.sc[0] = (float)__builtin_bit_cast(_Float16, scales[tile * kBlk + (lane >> 2)]);
+}
+
+// Exchange with lane ^ MASK exactly (every lane bit kept but MASK).
+template <int MASK>
+__device__ __forceinline__ float xchg_exact(float x) {
+    if constexpr (MASK == 8) return dpp_mov<kDppRowRor8>(x);       // (i + 8) mod 16 == i ^ 8
+    else return __shfl_xor(x, MASK, kWave);
+}
+
+// Transposed butterfly over lane bits BIT, BIT/2, .., 4 (the 16 groups of 4
+// lanes): v[0..N) are this lane's partial sums of N quantities; afterwards v[0]
+// holds the full sum of quantity lane >> 2 (N = 16).
+template <int N, int BIT>
+__device__ __forceinline__ void tbfly_blocks(float* v, int lane) {
+    if constexpr (BIT >= 4) {
+        constexpr int H = N / 2;
+        const bool up = (lane & BIT) != 0;
+#pragma unroll
+        for (int k = 0; k < H; ++k) {
+            const float keep = up ? v[H + k] : v[k];
+            const float send = up ? v[k] : v[H + k];
+            v[k] = keep + xchg_exact<BIT>(send);
+        }
+        tbfly_blocks<H, BIT / 2>(v, lane);
+    }
+}
+
 // Values per lane left by tbfly<N, BIT>, and the lane bits across which the
 // lanes hold copies of the same quantity (the steps that had one value left).
 constexpr int tb_count(int n, int bit) { return bit == 0 ? n : (n >= 2 ? tb_count((n + 1) / 2, bit / 2) : 1); }
@@ -315,9 +355,39 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
     // query fragment: this lane's columns of each head
     uint32_t qw[GT][C::WORDS];      // bf16 pairs (bf16 pools)
     uint32_t qb[GT][C::EPL / 2];    // bf16 pairs (INT8 pools with a bf16 query)
+    // keys-by-lane Q.K^T: head 4 nq + (lane & 3) at columns 8 (lane >> 2) .. +7
+    // (two MFMA B operands), and -128 x that head's query sum (the codes' bias)
+    constexpr bool MKQ = KV == KV_I8Q && D == 128;
+    constexpr int NHQQ = (GT + 3) / 4;
+    uint32_t qk[MKQ ? NHQQ : 1][4];
+    float qkb[MKQ ? NHQQ : 1];
     float qf[GT][C::EPL];           // fp32 (fp32 pools, INT8 pools with an fp32 query)
     float qsum[GT];
     auto load_q = [&](const Item& I) {
+        if constexpr (MKQ) {
+#pragma unroll
+            for (int nq = 0; nq < NHQQ; ++nq) {
+                const int j = 4 * nq + (lane & 3);
+                u32x4_t v = {0u, 0u, 0u, 0u};
+                if (j < I.nh)
+                    v = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.q) +
+                                                          ((int64_t)I.s * a.num_q_heads + I.h0 + j) * D +
+                                                          8 * (lane >> 2));
+                float t = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    qk[nq][i] = v[i];
+                    t += bf16lo(v[i]) + bf16hi(v[i]);
+                }
+                // sum over the 16 column blocks (lanes of the same head)
+                t += __shfl_xor(t, 4, kWave);
+                t += xchg_exact<8>(t);
+                t += __shfl_xor(t, 16, kWave);
+                t += __shfl_xor(t, 32, kWave);
+                qkb[nq] = -128.0f * t;
+            }
+            return;
+        }
 #pragma unroll
         for (int j = 0; j < GT; ++j) {
             const int64_t qoff = ((int64_t)I.s * a.num_q_heads + I.h0 + j) * D + col;
@@ -414,6 +484,10 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
     // compiler from sinking the load), so one to two tiles are always in flight
     // and there is no softmax phase to stall the stream: the softmax is online.
     Tile<KV, D, GT> tk, tv;
+    auto load_k = [&](Tile<KV, D, GT>& t, int64_t tile) {
+        if constexpr (KV == KV_I8Q && D == 128) load_tile_keys_by_lane<KV, D, GT>(t, a.k_pool, a.k_scale, tile, lane);
+        else load_tile<KV, D, GT>(t, a.k_pool, a.k_scale, tile, lane);
+    };
     float* lp = s_p[wave];
     int parity = 0;              // combine buffer of the current item
     Item I = item_info(blockIdx.x < total ? blockIdx.x : 0);
@@ -422,7 +496,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
         const int nbw0 = blocks_of_wave(I.t0, batch_end(I.t0, I.t1));
         install(ids_of(I, I.t0, nbw0));
         if (nbw0 > 0) {
-            load_tile<KV, D, GT>(tk, a.k_pool, a.k_scale, tile_of(0, I.g), lane);
+            load_k(tk, tile_of(0, I.g));
             load_tile<KV, D, GT>(tv, a.v_pool, a.v_scale, tile_of(0, I.g), lane);
         }
     }
@@ -449,6 +523,14 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
     constexpr bool MV = is_i8(KV) && D == 128;
     constexpr int NHQ = (GT + 3) / 4;            // groups of 4 heads
     const int hr = lane & 3;                     // this lane's head within a group
+    // INT8 pools with a bf16 query, head_dim 128: Q.K^T on the matrix cores too.
+    // The K tile comes in the keys-by-lane layout (load_tile_keys_by_lane), so
+    // in an MFMA block A = K (row r: key 4i + r over 4 columns), B = Q^T (column
+    // r: head 4 nq + r at the same columns), D = the 4 x 4 partial logits over
+    // the block's 8 columns; a transposed butterfly across the 16 blocks then
+    // leaves each lane one logit per head group: key lane >> 2, head 4 nq + hr.
+    constexpr bool MK = KV == KV_I8Q && D == 128;
+    constexpr int NS = MK ? NHQ : NT;            // logit slots per lane
 
     for (int item = blockIdx.x, following; item < total; item = following) {
         following = dyn ? __builtin_amdgcn_readfirstlane(s_next[parity ^ 1]) : item + (int)gridDim.x;
@@ -460,7 +542,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
 
         // running softmax state of this wave's keys: m per head (uniform), the
         // same m per logit slot of this lane, l per logit slot, acc per column
-        float m_run[GT], m_lane[NT], l_lane[NT], acc[GT][C::EPL], psum[GT];
+        float m_run[GT], m_lane[NS], l_lane[NS], acc[GT][C::EPL], psum[GT];
         f32x4_t accv[MV ? NHQ : 1][MV ? C::EPL : 1];  // MV: [head group][column] -> 4 heads
         float psl[MV ? NHQ : 1];                     // MV: weight sum of head 4 nq + hr, this lane's keys
 #pragma unroll
@@ -479,7 +561,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
             }
         }
 #pragma unroll
-        for (int kk = 0; kk < NT; ++kk) {
+        for (int kk = 0; kk < NS; ++kk) {
             m_lane[kk] = -INFINITY;
             l_lane[kk] = 0.0f;
         }
@@ -506,6 +588,80 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
             auto k_step = [&](const Tile<KV, D, GT>& t, int it) {
                 const int b = wave + kWaves * it;
                 const bool blk_ok = (okmask >> it) & 1;
+                if constexpr (MK) {
+                    f32x4_t dk[NHQ][4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        // the 8 biased codes u = q8 + 128 as bf16 (exact)
+                        uint32_t cw[4];
+#pragma unroll
+                        for (int w = 0; w < 2; ++w) {
+                            const uint32_t u = t.w[i].w[w] ^ 0x80808080u;
+                            const float f0 = (float)(u & 0xffu), f1 = (float)((u >> 8) & 0xffu);
+                            const float f2 = (float)((u >> 16) & 0xffu), f3 = (float)(u >> 24);
+                            cw[2 * w] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, f1),
+                                                              __builtin_bit_cast(uint32_t, f0), 0x07060302u);
+                            cw[2 * w + 1] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, f3),
+                                                                  __builtin_bit_cast(uint32_t, f2), 0x07060302u);
+                        }
+                        const bf16x4_t a0 = __builtin_bit_cast(bf16x4_t, u32x2_t{cw[0], cw[1]});
+                        const bf16x4_t a1 = __builtin_bit_cast(bf16x4_t, u32x2_t{cw[2], cw[3]});
+#pragma unroll
+                        for (int nq = 0; nq < NHQ; ++nq) {
+                            const bf16x4_t b0 = __builtin_bit_cast(bf16x4_t, u32x2_t{qk[nq][0], qk[nq][1]});
+                            const bf16x4_t b1 = __builtin_bit_cast(bf16x4_t, u32x2_t{qk[nq][2], qk[nq][3]});
+                            dk[nq][i] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(a0, b0, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f},
+                                                                               0, 0, 0);
+                            dk[nq][i] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(a1, b1, dk[nq][i], 0, 0, 0);
+                        }
+                    }
+                    // the lane's key and its visibility
+                    const int r = lane >> 2;
+                    const int tok = tbase + b * kBlk + r;
+                    const bool key_ok = blk_ok && tok >= c0 && tok < c1;
+                    float x[NHQ];
+                    bool over = false;
+#pragma unroll
+                    for (int nq = 0; nq < NHQ; ++nq) {
+                        float v[16];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+#pragma unroll
+                            for (int k2 = 0; k2 < 4; ++k2) v[4 * i + k2] = dk[nq][i][k2];
+                        tbfly_blocks<16, 32>(v, lane);
+                        const bool ok = key_ok && 4 * nq + hr < GT;
+                        x[nq] = ok ? (v[0] + qkb[nq]) * t.sc[0] * a.scale_log2 : -INFINITY;
+                        over |= x[nq] > m_lane[nq] + kRescale;
+                    }
+                    if (__builtin_amdgcn_ballot_w64(over) != 0) {
+#pragma unroll
+                        for (int j = 0; j < GT; ++j) {
+                            float v = -INFINITY;
+#pragma unroll
+                            for (int nq = 0; nq < NHQ; ++nq)
+                                if (4 * nq + hr == j) v = fmaxf(v, x[nq]);
+                            const float m_new = fmaxf(m_run[j], group_max<kWave>(v));
+                            const float alpha = (m_run[j] == -INFINITY) ? 0.0f : fast_exp2(m_run[j] - m_new);
+                            m_run[j] = m_new;
+#pragma unroll
+                            for (int e = 0; e < C::EPL; ++e) accv[j >> 2][e][j & 3] *= alpha;
+                            psl[j >> 2] *= hr == (j & 3) ? alpha : 1.0f;
+#pragma unroll
+                            for (int nq = 0; nq < NHQ; ++nq)
+                                if (4 * nq + hr == j) {
+                                    l_lane[nq] *= alpha;
+                                    m_lane[nq] = m_new;
+                                }
+                        }
+                    }
+#pragma unroll
+                    for (int nq = 0; nq < NHQ; ++nq) {
+                        const float p = (x[nq] == -INFINITY) ? 0.0f : fast_exp2(x[nq] - m_lane[nq]);
+                        l_lane[nq] += p;
+                        lp[r * C::GTP + 4 * nq + hr] = p;
+                    }
+                    return;
+                }
                 float part[C::NV];
 #pragma unroll
                 for (int i = 0; i < C::NLOAD; ++i) {
@@ -699,7 +855,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
             int it = 0;
             for (; it + 1 < nbw; ++it) {
                 k_step(tk, it);
-                load_tile<KV, D, GT>(tk, a.k_pool, a.k_scale, tile_of(it + 1, g), lane);
+                load_k(tk, tile_of(it + 1, g));
                 __builtin_amdgcn_sched_barrier(0);
                 v_step(tv, it);
                 load_tile<KV, D, GT>(tv, a.v_pool, a.v_scale, tile_of(it + 1, g), lane);
@@ -714,7 +870,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
             if (nbw > 0) k_step(tk, it);
             if (!more && have_next) load_q(NI);
             const int64_t t_n = (int64_t)__builtin_amdgcn_readlane(valid_id(id_n) ? id_n : 0, 0) * a.num_kv_heads + g_n;
-            load_tile<KV, D, GT>(tk, a.k_pool, a.k_scale, t_n, lane);
+            load_k(tk, t_n);
             __builtin_amdgcn_sched_barrier(0);
             if (nbw > 0) v_step(tv, it);
             load_tile<KV, D, GT>(tv, a.v_pool, a.v_scale, t_n, lane);
@@ -729,9 +885,15 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
 #pragma unroll
         for (int j = 0; j < GT; ++j) {
             float v = 0.0f;
+            if constexpr (MK) {
 #pragma unroll
-            for (int kk = 0; kk < NT; ++kk)
-                if (kk < tb_valid && (tb_base + kk) % GT == j) v += l_lane[kk];
+                for (int nq = 0; nq < NHQ; ++nq)
+                    if (4 * nq + hr == j) v += l_lane[nq];
+            } else {
+#pragma unroll
+                for (int kk = 0; kk < NT; ++kk)
+                    if (kk < tb_valid && (tb_base + kk) % GT == j) v += l_lane[kk];
+            }
             l_run[j] = group_sum<kWave>(v);
         }
         if constexpr (MV) {
