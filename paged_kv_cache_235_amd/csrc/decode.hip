@@ -184,19 +184,20 @@ __device__ __forceinline__ void load_tile(Tile<KV, D, GT>& t, const char* pool, 
     }
 }
 
-// An INT8 K tile (head_dim 128) laid out for Q.K^T on 4x4x4 MFMAs: load i
-// holds keys 4i .. 4i+3, lane l the 8 codes of key 4i + (l & 3) at columns
-// 8 (l >> 2) .. +7 (each load still reads one contiguous 512-byte run), so the
-// four lanes of an MFMA block hold four keys at the same columns; sc[0] is the
-// scale of key l >> 2, the key whose logit the lane ends up with.
+// A K tile (bf16 or INT8, head_dim 128) laid out for Q.K^T on 4x4x4 MFMAs:
+// load i holds keys 4i .. 4i+3, lane l the 8 elements of key 4i + (l & 3) at
+// columns 8 (l >> 2) .. +7 (each load still reads one contiguous run of four
+// rows), so the four lanes of an MFMA block hold four keys at the same
+// columns; INT8: sc[0] is the scale of key l >> 2, the key whose logit the
+// lane ends up with.
 template <int KV, int D, int GT>
 __device__ __forceinline__ void load_tile_keys_by_lane(Tile<KV, D, GT>& t, const char* pool,
                                                        const uint16_t* scales, int64_t tile, int lane) {
     using C = Cfg<KV, D, GT>;
-    const char* p = pool + tile * C::TILE_BYTES + (lane & 3) * C::ROW_BYTES + (lane >> 2) * 8;
+    const char* p = pool + tile * C::TILE_BYTES + (lane & 3) * C::ROW_BYTES + (lane >> 2) * C::LW;
 #pragma unroll
     for (int i = 0; i < C::NLOAD; ++i) t.w[i] = load_words<C::WORDS>(p + i * 4 * C::ROW_BYTES);
-    t.sc[0] = (float)__builtin_bit_cast(_Float16, scales[tile * kBlk + (lane >> 2)]);
+    if constexpr (is_i8(KV)) t.sc[0] = (float)__builtin_bit_cast(_Float16, scales[tile * kBlk + (lane >> 2)]);
 }
 
 // Exchange with lane ^ MASK exactly (every lane bit kept but MASK).
@@ -357,7 +358,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
     uint32_t qb[GT][C::EPL / 2];    // bf16 pairs (INT8 pools with a bf16 query)
     // keys-by-lane Q.K^T: head 4 nq + (lane & 3) at columns 8 (lane >> 2) .. +7
     // (two MFMA B operands), and -128 x that head's query sum (the codes' bias)
-    constexpr bool MKQ = KV == KV_I8Q && D == 128;
+    constexpr bool MKQ = (KV == KV_I8Q || (KV == KV_BF16 && GT > 4)) && D == 128;
     constexpr int NHQQ = (GT + 3) / 4;
     uint32_t qk[MKQ ? NHQQ : 1][4];
     float qkb[MKQ ? NHQQ : 1];
@@ -379,12 +380,16 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
                     qk[nq][i] = v[i];
                     t += bf16lo(v[i]) + bf16hi(v[i]);
                 }
-                // sum over the 16 column blocks (lanes of the same head)
-                t += __shfl_xor(t, 4, kWave);
-                t += xchg_exact<8>(t);
-                t += __shfl_xor(t, 16, kWave);
-                t += __shfl_xor(t, 32, kWave);
-                qkb[nq] = -128.0f * t;
+                if constexpr (KV == KV_I8Q) {
+                    // sum over the 16 column blocks (lanes of the same head)
+                    t += __shfl_xor(t, 4, kWave);
+                    t += xchg_exact<8>(t);
+                    t += __shfl_xor(t, 16, kWave);
+                    t += __shfl_xor(t, 32, kWave);
+                    qkb[nq] = -128.0f * t;
+                } else {
+                    qkb[nq] = 0.0f;
+                }
             }
             return;
         }
@@ -485,7 +490,8 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
     // and there is no softmax phase to stall the stream: the softmax is online.
     Tile<KV, D, GT> tk, tv;
     auto load_k = [&](Tile<KV, D, GT>& t, int64_t tile) {
-        if constexpr (KV == KV_I8Q && D == 128) load_tile_keys_by_lane<KV, D, GT>(t, a.k_pool, a.k_scale, tile, lane);
+        if constexpr ((KV == KV_I8Q || (KV == KV_BF16 && GT > 4)) && D == 128)
+            load_tile_keys_by_lane<KV, D, GT>(t, a.k_pool, a.k_scale, tile, lane);
         else load_tile<KV, D, GT>(t, a.k_pool, a.k_scale, tile, lane);
     };
     float* lp = s_p[wave];
@@ -520,7 +526,10 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
     // keys, as a bf16 value plus its bf16 remainder (two MFMAs, 16 bits of the
     // weight), D = that column's partial output for 4 heads.  The keys of the
     // other row groups are added in the combine, as for the FMA form.
-    constexpr bool MV = is_i8(KV) && D == 128;
+    // bf16 pools take the MFMA forms only with more than 4 heads per item: at 4
+    // (the HBM-bound large batches) the MFMA-and-butterfly chain measured ~0.5%
+    // slower than the FMA form, at 6 (latency-bound small batches) 3-5% faster
+    constexpr bool MV = (is_i8(KV) || (KV == KV_BF16 && GT > 4)) && D == 128;
     constexpr int NHQ = (GT + 3) / 4;            // groups of 4 heads
     const int hr = lane & 3;                     // this lane's head within a group
     // INT8 pools with a bf16 query, head_dim 128: Q.K^T on the matrix cores too.
@@ -529,7 +538,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
     // r: head 4 nq + r at the same columns), D = the 4 x 4 partial logits over
     // the block's 8 columns; a transposed butterfly across the 16 blocks then
     // leaves each lane one logit per head group: key lane >> 2, head 4 nq + hr.
-    constexpr bool MK = KV == KV_I8Q && D == 128;
+    constexpr bool MK = (KV == KV_I8Q || (KV == KV_BF16 && GT > 4)) && D == 128;
     constexpr int NS = MK ? NHQ : NT;            // logit slots per lane
 
     for (int item = blockIdx.x, following; item < total; item = following) {
@@ -592,8 +601,13 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
                     f32x4_t dk[NHQ][4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        // the 8 biased codes u = q8 + 128 as bf16 (exact)
+                        // bf16 pools: the row's 8 elements as they are; INT8: the
+                        // 8 biased codes u = q8 + 128 as bf16 (exact)
                         uint32_t cw[4];
+                        if constexpr (KV == KV_BF16) {
+#pragma unroll
+                            for (int w = 0; w < 4; ++w) cw[w] = t.w[i].w[w];
+                        } else
 #pragma unroll
                         for (int w = 0; w < 2; ++w) {
                             const uint32_t u = t.w[i].w[w] ^ 0x80808080u;
@@ -630,7 +644,8 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
                             for (int k2 = 0; k2 < 4; ++k2) v[4 * i + k2] = dk[nq][i][k2];
                         tbfly_blocks<16, 32>(v, lane);
                         const bool ok = key_ok && 4 * nq + hr < GT;
-                        x[nq] = ok ? (v[0] + qkb[nq]) * t.sc[0] * a.scale_log2 : -INFINITY;
+                        const float sc = is_i8(KV) ? t.sc[0] : 1.0f;
+                        x[nq] = ok ? (v[0] + qkb[nq]) * sc * a.scale_log2 : -INFINITY;
                         over |= x[nq] > m_lane[nq] + kRescale;
                     }
                     if (__builtin_amdgcn_ballot_w64(over) != 0) {
@@ -645,7 +660,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
                             m_run[j] = m_new;
 #pragma unroll
                             for (int e = 0; e < C::EPL; ++e) accv[j >> 2][e][j & 3] *= alpha;
-                            psl[j >> 2] *= hr == (j & 3) ? alpha : 1.0f;
+                            if constexpr (is_i8(KV)) psl[j >> 2] *= hr == (j & 3) ? alpha : 1.0f;
 #pragma unroll
                             for (int nq = 0; nq < NHQ; ++nq)
                                 if (4 * nq + hr == j) {
@@ -739,7 +754,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
                         if constexpr (MV) {
 #pragma unroll
                             for (int e = 0; e < C::EPL; ++e) accv[j >> 2][e][j & 3] *= alpha;
-                            psl[j >> 2] *= hr == (j & 3) ? alpha : 1.0f;
+                            if constexpr (is_i8(KV)) psl[j >> 2] *= hr == (j & 3) ? alpha : 1.0f;
                         } else {
                             psum[j] *= alpha;
 #pragma unroll
@@ -784,14 +799,45 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
                             const int tok = tbase + b * kBlk + r;
                             const bool row_ok = full || (blk_ok && tok >= c0 && tok < c1);
                             const float pj = lp[r * C::GTP + (j < GT ? j : 0)];
-                            w[i] = (row_ok && j < GT) ? pj * t.sc[i] : 0.0f;
-                            psl[nq] += w[i];
+                            if constexpr (is_i8(KV)) {
+                                w[i] = (row_ok && j < GT) ? pj * t.sc[i] : 0.0f;
+                                psl[nq] += w[i];
+                            } else {
+                                w[i] = (row_ok && j < GT) ? pj : 0.0f;
+                            }
                         }
                         const uint32_t h01 = pack_bf16x2(w[0], w[1]), h23 = pack_bf16x2(w[2], w[3]);
                         const uint32_t l01 = pack_bf16x2(w[0] - bf16lo(h01), w[1] - bf16hi(h01));
                         const uint32_t l23 = pack_bf16x2(w[2] - bf16lo(h23), w[3] - bf16hi(h23));
                         a_hi[nq] = __builtin_bit_cast(bf16x4_t, u32x2_t{h01, h23});
                         a_lo[nq] = __builtin_bit_cast(bf16x4_t, u32x2_t{l01, l23});
+                    }
+                    if constexpr (KV == KV_BF16) {
+                        // B: column e of keys 4t + q; rows past the keys zeroed on an
+                        // edge tile (they may hold NaN, and 0 x NaN is NaN)
+                        uint32_t vw[4][4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int r = i * C::RPL + row_lane;
+                            const int tok = tbase + b * kBlk + r;
+                            const bool row_ok = full || (blk_ok && tok >= c0 && tok < c1);
+#pragma unroll
+                            for (int wd = 0; wd < 4; ++wd) vw[i][wd] = (full || row_ok) ? t.w[i].w[wd] : 0u;
+                        }
+#pragma unroll
+                        for (int e = 0; e < C::EPL; ++e) {
+                            const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+                            const uint32_t b01 = __builtin_amdgcn_perm(vw[1][e >> 1], vw[0][e >> 1], sel);
+                            const uint32_t b23 = __builtin_amdgcn_perm(vw[3][e >> 1], vw[2][e >> 1], sel);
+                            const bf16x4_t bv = __builtin_bit_cast(bf16x4_t, u32x2_t{b01, b23});
+#pragma unroll
+                            for (int nq = 0; nq < NHQ; ++nq)
+                                accv[nq][e] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(a_hi[nq], bv, accv[nq][e], 0, 0, 0);
+#pragma unroll
+                            for (int nq = 0; nq < NHQ; ++nq)
+                                accv[nq][e] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(a_lo[nq], bv, accv[nq][e], 0, 0, 0);
+                        }
+                        return;
                     }
                     // B: column e's biased codes u = q8 + 128 at keys 4t + q, as bf16
                     uint32_t u[4][2];
@@ -897,10 +943,12 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
             l_run[j] = group_sum<kWave>(v);
         }
         if constexpr (MV) {
-            // heads' weight sums for this lane's keys: lane (lane & ~3) + (j & 3)
-            // holds head j's
+            // INT8: heads' weight sums for this lane's keys: lane (lane & ~3) +
+            // (j & 3) holds head j's
+            if constexpr (is_i8(KV)) {
 #pragma unroll
-            for (int j = 0; j < GT; ++j) psum[j] = __shfl(psl[j >> 2], (lane & ~3) | (j & 3), kWave);
+                for (int j = 0; j < GT; ++j) psum[j] = __shfl(psl[j >> 2], (lane & ~3) | (j & 3), kWave);
+            }
 #pragma unroll
             for (int j = 0; j < GT; ++j)
 #pragma unroll
