@@ -75,6 +75,26 @@ def test_group_sizes_and_head_dims(hq, hkv, d, dt):
     assert_close(out, expected_outputs(case), dt)
 
 
+I8_GEOMS = [  # Hq, Hkv: query heads per KV head 1, 2, 3, 5, 8 at head_dim 128
+    (4, 4), (8, 4), (9, 3), (10, 2), (16, 2),
+]
+
+
+@pytest.mark.parametrize("q_dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("hq,hkv", I8_GEOMS, ids=[f"{g[0]}q{g[1]}kv" for g in I8_GEOMS])
+def test_int8_group_sizes_at_head_dim_128(hq, hkv, q_dtype):
+    """INT8 pools at head_dim 128 for every group width the kernels handle in
+    groups of four heads (fewer than four, more than four, two groups), with
+    ragged lengths across 512-token partitions, single-pass and split."""
+    lens = [1, 2, 16, 17, 511, 512, 513, 1030]
+    case = workloads.make_case("i8geom", 74, lens, [1] * len(lens), hq, hkv, 128, in_dtype=q_dtype,
+                               kv_dtype="i8", outliers=0.01)
+    ref = expected_outputs(case)
+    for part in (0, 512):
+        out, _ = _gpu(case, partition_size=part)
+        assert_close(out, ref, "bf16", f"{q_dtype} P={part}")
+
+
 @pytest.mark.parametrize("window", [1, 7, 16, 500, 4096])
 @pytest.mark.parametrize("part", [0, 16, 512])
 def test_sliding_window(window, part):
