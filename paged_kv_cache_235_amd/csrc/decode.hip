@@ -200,6 +200,38 @@ __device__ __forceinline__ void load_tile_keys_by_lane(Tile<KV, D, GT>& t, const
     if constexpr (is_i8(KV)) t.sc[0] = (float)__builtin_bit_cast(_Float16, scales[tile * kBlk + (lane >> 2)]);
 }
 
+// The key whose logit lane l holds after the INT8 wide-load Q.K^T: key bits
+// 0-1 are lane bits 2-3, key bit 2 is lane bit 5, key bit 3 is lane bit 4.
+__device__ __forceinline__ int wide_key(int lane) {
+    return ((lane >> 2) & 3) | ((lane >> 3) & 4) | ((lane >> 1) & 8);
+}
+
+// An INT8 K tile (head_dim 128) for Q.K^T on 4x4x4 MFMAs with 16-byte loads:
+// load i holds keys 8i .. 8i+7 (one contiguous 1 KiB run), lane l the 16 codes
+// of key 8i + 4 (l >> 5) + (l & 3) at columns 16 ((l >> 2) & 7) .. +15, in
+// w[2i] (columns +0..7) and w[2i+1] (+8..15); so the four lanes of an MFMA
+// block hold four keys at the same columns.  sc[0] is the scale of key
+// wide_key(l), the key whose logit the lane ends up with.  Rows reached by
+// lanes in four different 128-byte rows per quad cost less at 16 bytes per
+// lane than at 8.
+template <int KV, int D, int GT>
+__device__ __forceinline__ void load_tile_keys_wide(Tile<KV, D, GT>& t, const char* pool,
+                                                    const uint16_t* scales, int64_t tile, int lane) {
+    using C = Cfg<KV, D, GT>;
+    static_assert(KV == KV_I8Q && D == 128 && C::NLOAD == 4 && C::WORDS == 2, "INT8 rows of 128 codes");
+    const char* p = pool + tile * C::TILE_BYTES + (4 * (lane >> 5) + (lane & 3)) * C::ROW_BYTES +
+                    16 * ((lane >> 2) & 7);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p + i * 8 * C::ROW_BYTES));
+        t.w[2 * i].w[0] = v[0];
+        t.w[2 * i].w[1] = v[1];
+        t.w[2 * i + 1].w[0] = v[2];
+        t.w[2 * i + 1].w[1] = v[3];
+    }
+    t.sc[0] = (float)__builtin_bit_cast(_Float16, scales[tile * kBlk + wide_key(lane)]);
+}
+
 // Exchange with lane ^ MASK exactly (every lane bit kept but MASK).
 template <int MASK>
 __device__ __forceinline__ float xchg_exact(float x) {
@@ -360,12 +392,42 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
     // (two MFMA B operands), and -128 x that head's query sum (the codes' bias)
     constexpr bool MKQ = (KV == KV_I8Q || (KV == KV_BF16 && GT > 4)) && D == 128;
     constexpr int NHQQ = (GT + 3) / 4;
-    uint32_t qk[MKQ ? NHQQ : 1][4];
+    // INT8 pools with a bf16 query, head_dim 128: K tiles come with 16-byte
+    // loads (load_tile_keys_wide), and the query fragment is head 4 nq +
+    // (lane & 3) at columns 16 ((lane >> 2) & 7) .. +15 (four B operands)
+    constexpr bool KW = KV == KV_I8Q && D == 128;
+    uint32_t qk[MKQ ? NHQQ : 1][KW ? 8 : 4];
     float qkb[MKQ ? NHQQ : 1];
     float qf[GT][C::EPL];           // fp32 (fp32 pools, INT8 pools with an fp32 query)
     float qsum[GT];
     auto load_q = [&](const Item& I) {
-        if constexpr (MKQ) {
+        if constexpr (KW) {
+#pragma unroll
+            for (int nq = 0; nq < NHQQ; ++nq) {
+                const int j = 4 * nq + (lane & 3);
+                u32x4_t v0 = {0u, 0u, 0u, 0u}, v1 = {0u, 0u, 0u, 0u};
+                if (j < I.nh) {
+                    const u32x4_t* qp = reinterpret_cast<const u32x4_t*>(
+                        static_cast<const uint16_t*>(a.q) + ((int64_t)I.s * a.num_q_heads + I.h0 + j) * D +
+                        16 * ((lane >> 2) & 7));
+                    v0 = qp[0];
+                    v1 = qp[1];
+                }
+                float t = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    qk[nq][i] = v0[i];
+                    qk[nq][4 + i] = v1[i];
+                    t += bf16lo(v0[i]) + bf16hi(v0[i]) + bf16lo(v1[i]) + bf16hi(v1[i]);
+                }
+                // sum over the 8 column chunks (lane bits 2-4; bit 5 holds copies)
+                t += __shfl_xor(t, 4, kWave);
+                t += xchg_exact<8>(t);
+                t += __shfl_xor(t, 16, kWave);
+                qkb[nq] = -128.0f * t;
+            }
+            return;
+        } else if constexpr (MKQ) {
 #pragma unroll
             for (int nq = 0; nq < NHQQ; ++nq) {
                 const int j = 4 * nq + (lane & 3);
@@ -490,7 +552,9 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
     // and there is no softmax phase to stall the stream: the softmax is online.
     Tile<KV, D, GT> tk, tv;
     auto load_k = [&](Tile<KV, D, GT>& t, int64_t tile) {
-        if constexpr ((KV == KV_I8Q || (KV == KV_BF16 && GT > 4)) && D == 128)
+        if constexpr (KW)
+            load_tile_keys_wide<KV, D, GT>(t, a.k_pool, a.k_scale, tile, lane);
+        else if constexpr (MKQ)
             load_tile_keys_by_lane<KV, D, GT>(t, a.k_pool, a.k_scale, tile, lane);
         else load_tile<KV, D, GT>(t, a.k_pool, a.k_scale, tile, lane);
     };
@@ -591,12 +655,95 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
             const int id_n = ids_of(J, jc0, nbw_n);
             const int g_n = J.g;
 
+            // MFMA Q.K^T: this lane's logits x[nq] (key r, head 4 nq + hr) into
+            // the online softmax (rescale only when one passes the running
+            // maximum by more than 2^kRescale), probabilities to LDS
+            auto softmax_update = [&](const float* x, bool over, int r) {
+                if constexpr (MK) {
+                    if (__builtin_amdgcn_ballot_w64(over) != 0) {
+#pragma unroll
+                        for (int j = 0; j < GT; ++j) {
+                            float v = -INFINITY;
+#pragma unroll
+                            for (int nq = 0; nq < NHQ; ++nq)
+                                if (4 * nq + hr == j) v = fmaxf(v, x[nq]);
+                            const float m_new = fmaxf(m_run[j], group_max<kWave>(v));
+                            const float alpha = (m_run[j] == -INFINITY) ? 0.0f : fast_exp2(m_run[j] - m_new);
+                            m_run[j] = m_new;
+#pragma unroll
+                            for (int e = 0; e < C::EPL; ++e) accv[j >> 2][e][j & 3] *= alpha;
+                            if constexpr (is_i8(KV)) psl[j >> 2] *= hr == (j & 3) ? alpha : 1.0f;
+#pragma unroll
+                            for (int nq = 0; nq < NHQ; ++nq)
+                                if (4 * nq + hr == j) {
+                                    l_lane[nq] *= alpha;
+                                    m_lane[nq] = m_new;
+                                }
+                        }
+                    }
+#pragma unroll
+                    for (int nq = 0; nq < NHQ; ++nq) {
+                        const float p = (x[nq] == -INFINITY) ? 0.0f : fast_exp2(x[nq] - m_lane[nq]);
+                        l_lane[nq] += p;
+                        lp[r * C::GTP + 4 * nq + hr] = p;
+                    }
+                }
+            };
+
             // ---- K tile -> logits of its 16 keys for every head, online softmax
             // update (rescale only when a logit passes the running maximum by
             // more than 2^kRescale), probabilities to LDS
             auto k_step = [&](const Tile<KV, D, GT>& t, int it) {
                 const int b = wave + kWaves * it;
                 const bool blk_ok = (okmask >> it) & 1;
+                if constexpr (KW) {
+                    // INT8, 16-byte K loads: per load i, four MFMAs (one per 4
+                    // columns of the lane's 16) give keys 8i + 4 (lane >> 5) + r'
+                    // x heads 4 nq + r over the lane's column chunk
+                    f32x4_t dk[NHQ][2];
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+                        for (int nq = 0; nq < NHQ; ++nq) dk[nq][i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                        for (int m = 0; m < 4; ++m) {
+                            // four biased codes u = q8 + 128 as bf16 (exact)
+                            const uint32_t u = t.w[2 * i + (m >> 1)].w[m & 1] ^ 0x80808080u;
+                            const float f0 = (float)(u & 0xffu), f1 = (float)((u >> 8) & 0xffu);
+                            const float f2 = (float)((u >> 16) & 0xffu), f3 = (float)(u >> 24);
+                            const uint32_t c01 = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, f1),
+                                                                       __builtin_bit_cast(uint32_t, f0), 0x07060302u);
+                            const uint32_t c23 = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, f3),
+                                                                       __builtin_bit_cast(uint32_t, f2), 0x07060302u);
+                            const bf16x4_t am = __builtin_bit_cast(bf16x4_t, u32x2_t{c01, c23});
+#pragma unroll
+                            for (int nq = 0; nq < NHQ; ++nq) {
+                                const bf16x4_t bm =
+                                    __builtin_bit_cast(bf16x4_t, u32x2_t{qk[nq][2 * m], qk[nq][2 * m + 1]});
+                                dk[nq][i] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(am, bm, dk[nq][i], 0, 0, 0);
+                            }
+                        }
+                    }
+                    const int r = wide_key(lane);
+                    const int tok = tbase + b * kBlk + r;
+                    const bool key_ok = blk_ok && tok >= c0 && tok < c1;
+                    float x[NHQ];
+                    bool over = false;
+#pragma unroll
+                    for (int nq = 0; nq < NHQ; ++nq) {
+                        float v[8];
+#pragma unroll
+                        for (int i = 0; i < 2; ++i)
+#pragma unroll
+                            for (int k2 = 0; k2 < 4; ++k2) v[4 * i + k2] = dk[nq][i][k2];
+                        tbfly_blocks<8, 16>(v, lane);
+                        const bool ok = key_ok && 4 * nq + hr < GT;
+                        x[nq] = ok ? (v[0] + qkb[nq]) * t.sc[0] * a.scale_log2 : -INFINITY;
+                        over |= x[nq] > m_lane[nq] + kRescale;
+                    }
+                    softmax_update(x, over, r);
+                    return;
+                }
                 if constexpr (MK) {
                     f32x4_t dk[NHQ][4];
 #pragma unroll
@@ -648,33 +795,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
                         x[nq] = ok ? (v[0] + qkb[nq]) * sc * a.scale_log2 : -INFINITY;
                         over |= x[nq] > m_lane[nq] + kRescale;
                     }
-                    if (__builtin_amdgcn_ballot_w64(over) != 0) {
-#pragma unroll
-                        for (int j = 0; j < GT; ++j) {
-                            float v = -INFINITY;
-#pragma unroll
-                            for (int nq = 0; nq < NHQ; ++nq)
-                                if (4 * nq + hr == j) v = fmaxf(v, x[nq]);
-                            const float m_new = fmaxf(m_run[j], group_max<kWave>(v));
-                            const float alpha = (m_run[j] == -INFINITY) ? 0.0f : fast_exp2(m_run[j] - m_new);
-                            m_run[j] = m_new;
-#pragma unroll
-                            for (int e = 0; e < C::EPL; ++e) accv[j >> 2][e][j & 3] *= alpha;
-                            if constexpr (is_i8(KV)) psl[j >> 2] *= hr == (j & 3) ? alpha : 1.0f;
-#pragma unroll
-                            for (int nq = 0; nq < NHQ; ++nq)
-                                if (4 * nq + hr == j) {
-                                    l_lane[nq] *= alpha;
-                                    m_lane[nq] = m_new;
-                                }
-                        }
-                    }
-#pragma unroll
-                    for (int nq = 0; nq < NHQ; ++nq) {
-                        const float p = (x[nq] == -INFINITY) ? 0.0f : fast_exp2(x[nq] - m_lane[nq]);
-                        l_lane[nq] += p;
-                        lp[r * C::GTP + 4 * nq + hr] = p;
-                    }
+                    softmax_update(x, over, r);
                     return;
                 }
                 float part[C::NV];
