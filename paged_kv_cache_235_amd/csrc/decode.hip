@@ -239,12 +239,34 @@ __device__ __forceinline__ float xchg_exact(float x) {
     else return __shfl_xor(x, MASK, kWave);
 }
 
+// One step of a transposed butterfly across lane bit 16 or 32 in one
+// instruction: lo holds quantities the lanes without the bit keep, hi those the
+// lanes with it keep.  v_permlane16_swap exchanges the odd 16-lane rows of its
+// first operand with the even rows of its second (v_permlane32_swap: the upper
+// half of the first with the lower half of the second), after which lo + hi is
+// the kept quantity plus the partner lane's copy of it, in every lane.  (Inline
+// asm: the compiler's builtin for these swaps returns the first register twice.)
+template <int BIT>
+__device__ __forceinline__ float swap_add(float lo, float hi) {
+    static_assert(BIT == 16 || BIT == 32, "lane bit of a permlane swap");
+    if constexpr (BIT == 16)
+        asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(lo), "+v"(hi));
+    else
+        asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(lo), "+v"(hi));
+    return lo + hi;
+}
+
 // Transposed butterfly over lane bits BIT, BIT/2, .., 4 (the 16 groups of 4
 // lanes): v[0..N) are this lane's partial sums of N quantities; afterwards v[0]
 // holds the full sum of quantity lane >> 2 (N = 16).
 template <int N, int BIT>
 __device__ __forceinline__ void tbfly_blocks(float* v, int lane) {
-    if constexpr (BIT >= 4) {
+    if constexpr (BIT >= 16) {
+        constexpr int H = N / 2;
+#pragma unroll
+        for (int k = 0; k < H; ++k) v[k] = swap_add<BIT>(v[k], v[H + k]);
+        tbfly_blocks<H, BIT / 2>(v, lane);
+    } else if constexpr (BIT >= 4) {
         constexpr int H = N / 2;
         const bool up = (lane & BIT) != 0;
 #pragma unroll
