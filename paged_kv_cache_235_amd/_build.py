@@ -42,8 +42,11 @@ def hipcc() -> str:
 
 # per-file flags.  decode.hip: its MFMA accumulators (INT8 P.V) in ordinary
 # VGPRs rather than accumulation registers, which keeps the INT8 decode kernel
-# at three waves per SIMD (164 registers at 4 heads per item instead of 200).
-FILE_FLAGS = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# at three waves per SIMD (164 registers at 4 heads per item instead of 200);
+# and no atomic optimizer: its one atomic with a result (a work-counter claim
+# by a single lane) would become a wave scan that reads the result at once,
+# which makes the wave wait there for every load it has in flight.
+FILE_FLAGS = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
 
 
 def _compile(src: str) -> str:

@@ -99,11 +99,26 @@ struct Cfg {
 __device__ __forceinline__ int seq_off(const DecodeArgs& a, int s) {
     return a.table_offsets ? max(0, a.table_offsets[s]) : 0;
 }
+// The same for a wave-uniform s, through the scalar cache (a vector load here
+// would make the wave wait for every load it has in flight).
+__device__ __forceinline__ int seq_off_uniform(const DecodeArgs& a, int s) {
+    if (!a.table_offsets) return 0;
+    const __attribute__((address_space(4))) int32_t* t =
+        (const __attribute__((address_space(4))) int32_t*)a.table_offsets;
+    return max(0, t[s]);
+}
 // the context length, clamped to what the table row can address
-__device__ __forceinline__ int seq_len(const DecodeArgs& a, int s) {
-    const int L = a.context_lens[s];
-    const int64_t cap = ((int64_t)a.max_blocks + seq_off(a, s)) * kBlk;
+__device__ __forceinline__ int clamp_len(const DecodeArgs& a, int L, int off) {
+    const int64_t cap = ((int64_t)a.max_blocks + off) * kBlk;
     return L < 0 ? 0 : (L > cap ? (int)cap : L);
+}
+__device__ __forceinline__ int seq_len(const DecodeArgs& a, int s) {
+    return clamp_len(a, a.context_lens[s], seq_off(a, s));
+}
+__device__ __forceinline__ int seq_len_uniform(const DecodeArgs& a, int s) {
+    const __attribute__((address_space(4))) int32_t* t =
+        (const __attribute__((address_space(4))) int32_t*)a.context_lens;
+    return clamp_len(a, t[s], seq_off_uniform(a, s));
 }
 // First visible key: the window's start, and never before the row's first
 // block (keys of released blocks do not exist for the kernels), so the keys of
@@ -164,10 +179,12 @@ __device__ __forceinline__ void widen(const Words<WORDS>& t, float* x) {
 
 // One (block, KV head) tile as this lane holds it: NLOAD 16- or 8-byte pieces
 // (rows i * RPL + lane / LPR), plus the rows' INT8 scales.
+// The scales stay binary16 until a step uses them: converted next to their
+// load, they would make the wave wait there for every load issued before them.
 template <int KV, int D, int GT>
 struct Tile {
     Words<Cfg<KV, D, GT>::WORDS> w[Cfg<KV, D, GT>::NLOAD];
-    float sc[Cfg<KV, D, GT>::NLOAD];
+    _Float16 sc[Cfg<KV, D, GT>::NLOAD];
 };
 
 template <int KV, int D, int GT>
@@ -180,7 +197,7 @@ __device__ __forceinline__ void load_tile(Tile<KV, D, GT>& t, const char* pool, 
     if constexpr (is_i8(KV)) {
 #pragma unroll
         for (int i = 0; i < C::NLOAD; ++i)
-            t.sc[i] = (float)__builtin_bit_cast(_Float16, scales[tile * kBlk + i * C::RPL + lane / C::LPR]);
+            t.sc[i] = __builtin_bit_cast(_Float16, scales[tile * kBlk + i * C::RPL + lane / C::LPR]);
     }
 }
 
@@ -197,7 +214,7 @@ __device__ __forceinline__ void load_tile_keys_by_lane(Tile<KV, D, GT>& t, const
     const char* p = pool + tile * C::TILE_BYTES + (lane & 3) * C::ROW_BYTES + (lane >> 2) * C::LW;
 #pragma unroll
     for (int i = 0; i < C::NLOAD; ++i) t.w[i] = load_words<C::WORDS>(p + i * 4 * C::ROW_BYTES);
-    if constexpr (is_i8(KV)) t.sc[0] = (float)__builtin_bit_cast(_Float16, scales[tile * kBlk + (lane >> 2)]);
+    if constexpr (is_i8(KV)) t.sc[0] = __builtin_bit_cast(_Float16, scales[tile * kBlk + (lane >> 2)]);
 }
 
 // The key whose logit lane l holds after the INT8 wide-load Q.K^T: key bits
@@ -229,7 +246,7 @@ __device__ __forceinline__ void load_tile_keys_wide(Tile<KV, D, GT>& t, const ch
         t.w[2 * i + 1].w[0] = v[2];
         t.w[2 * i + 1].w[1] = v[3];
     }
-    t.sc[0] = (float)__builtin_bit_cast(_Float16, scales[tile * kBlk + wide_key(lane)]);
+    t.sc[0] = __builtin_bit_cast(_Float16, scales[tile * kBlk + wide_key(lane)]);
 }
 
 // Exchange with lane ^ MASK exactly (every lane bit kept but MASK).
@@ -375,7 +392,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
         if constexpr (direct) {
             // one item per (sequence, KV head, head chunk), keys from 0 to L
             I.s = gp;
-            L = seq_len(a, I.s);
+            L = seq_len_uniform(a, I.s);
             I.nparts = 1;
             I.k = I.kr = 0;
             I.off = 0;
@@ -395,11 +412,12 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
             I.nparts = uni(s_prefix[I.s + 1]) - ps;
             L = uni(s_len[I.s]);
         }
-        const int lo = min(first_key(a, L, uni(seq_off(a, I.s))), L);
+        const int off = seq_off_uniform(a, I.s);
+        const int lo = min(first_key(a, L, off), L);
         const int P = a.part_tokens;
         I.k = (P > 0 ? lo / P : 0) + (gp - ps);
         I.kr = gp - ps;
-        I.off = uni(seq_off(a, I.s));
+        I.off = off;
         I.t0 = P > 0 ? max(lo, I.k * P) : lo;
         I.t1 = P > 0 ? min(L, (I.k + 1) * P) : L;
         I.h0 = I.g * a.group + hchunk * GT;         // first query head of the item
@@ -422,6 +440,10 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
     float qkb[MKQ ? NHQQ : 1];
     float qf[GT][C::EPL];           // fp32 (fp32 pools, INT8 pools with an fp32 query)
     float qsum[GT];
+    // The query's loads are issued during the previous item's last batch; what
+    // is derived from them (the sums that remove the INT8 codes' bias) waits
+    // for finish_q at the top of the item, where the loads of the item's first
+    // tiles, issued after the query's, may still be in flight.
     auto load_q = [&](const Item& I) {
         if constexpr (KW) {
 #pragma unroll
@@ -435,18 +457,11 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
                     v0 = qp[0];
                     v1 = qp[1];
                 }
-                float t = 0.0f;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     qk[nq][i] = v0[i];
                     qk[nq][4 + i] = v1[i];
-                    t += bf16lo(v0[i]) + bf16hi(v0[i]) + bf16lo(v1[i]) + bf16hi(v1[i]);
                 }
-                // sum over the 8 column chunks (lane bits 2-4; bit 5 holds copies)
-                t += __shfl_xor(t, 4, kWave);
-                t += xchg_exact<8>(t);
-                t += __shfl_xor(t, 16, kWave);
-                qkb[nq] = -128.0f * t;
             }
             return;
         } else if constexpr (MKQ) {
@@ -458,29 +473,14 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
                     v = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.q) +
                                                           ((int64_t)I.s * a.num_q_heads + I.h0 + j) * D +
                                                           8 * (lane >> 2));
-                float t = 0.0f;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    qk[nq][i] = v[i];
-                    t += bf16lo(v[i]) + bf16hi(v[i]);
-                }
-                if constexpr (KV == KV_I8Q) {
-                    // sum over the 16 column blocks (lanes of the same head)
-                    t += __shfl_xor(t, 4, kWave);
-                    t += xchg_exact<8>(t);
-                    t += __shfl_xor(t, 16, kWave);
-                    t += __shfl_xor(t, 32, kWave);
-                    qkb[nq] = -128.0f * t;
-                } else {
-                    qkb[nq] = 0.0f;
-                }
+                for (int i = 0; i < 4; ++i) qk[nq][i] = v[i];
             }
             return;
         }
 #pragma unroll
         for (int j = 0; j < GT; ++j) {
             const int64_t qoff = ((int64_t)I.s * a.num_q_heads + I.h0 + j) * D + col;
-            qsum[j] = 0.0f;
             if constexpr (KV == KV_BF16) {
                 Words<4> t{};
                 if (j < I.nh) {
@@ -493,10 +493,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
                 u32x4_t v = {0u, 0u, 0u, 0u};
                 if (j < I.nh) v = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a.q) + qoff);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    qb[j][i] = v[i];
-                    qsum[j] += bf16lo(v[i]) + bf16hi(v[i]);
-                }
+                for (int i = 0; i < 4; ++i) qb[j][i] = v[i];
             } else {
 #pragma unroll
                 for (int e = 0; e < C::EPL; ++e) {
@@ -505,8 +502,52 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
                         x = a.q_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(a.q)[qoff + e])
                                      : static_cast<const float*>(a.q)[qoff + e];
                     qf[j][e] = x;
-                    qsum[j] += x;
                 }
+            }
+        }
+    };
+    auto finish_q = [&]() {
+        if constexpr (KW) {
+#pragma unroll
+            for (int nq = 0; nq < NHQQ; ++nq) {
+                float t = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) t += bf16lo(qk[nq][i]) + bf16hi(qk[nq][i]);
+                // sum over the 8 column chunks (lane bits 2-4; bit 5 holds copies)
+                t += __shfl_xor(t, 4, kWave);
+                t += xchg_exact<8>(t);
+                t += __shfl_xor(t, 16, kWave);
+                qkb[nq] = -128.0f * t;
+            }
+        } else if constexpr (MKQ) {
+#pragma unroll
+            for (int nq = 0; nq < NHQQ; ++nq) {
+                if constexpr (KV == KV_I8Q) {
+                    float t = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) t += bf16lo(qk[nq][i]) + bf16hi(qk[nq][i]);
+                    // sum over the 16 column blocks (lanes of the same head)
+                    t += __shfl_xor(t, 4, kWave);
+                    t += xchg_exact<8>(t);
+                    t += __shfl_xor(t, 16, kWave);
+                    t += __shfl_xor(t, 32, kWave);
+                    qkb[nq] = -128.0f * t;
+                } else {
+                    qkb[nq] = 0.0f;
+                }
+            }
+        } else if constexpr (is_i8(KV)) {
+#pragma unroll
+            for (int j = 0; j < GT; ++j) {
+                float t = 0.0f;
+                if constexpr (KV == KV_I8Q) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) t += bf16lo(qb[j][i]) + bf16hi(qb[j][i]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < C::EPL; ++e) t += qf[j][e];
+                }
+                qsum[j] = t;
             }
         }
     };
@@ -532,6 +573,10 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
         return id;
     };
     auto valid_id = [&](int id) { return id >= 0 && id < a.num_blocks; };
+    // the block tables through the constant address space: wave-uniform reads
+    // become scalar loads
+    const __attribute__((address_space(4))) int32_t* s_table =
+        (const __attribute__((address_space(4))) int32_t*)a.block_tables;
     auto install = [&](int id) {
         const bool ok = valid_id(id);
         lid = ok ? id : 0;
@@ -553,17 +598,24 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
     // the same blocks).  The item after the current one is known an item ahead
     // (s_next), so its loads can start before the current item is combined.
     const bool dyn = a.ticket != nullptr;
-    // one claim on the counter; the claim that returns total - 1 is the last one
-    // of the launch (each workgroup claims until it passes the last item, so
-    // claims 0 .. total - 1 are made), and it leaves the counter at zero for the
-    // next launch that uses this workspace
-    auto claim = [&]() {
-        const unsigned c = atomicAdd(a.ticket, 1u);
-        if (c == (unsigned)total - 1u) atomicExch(a.ticket, 0u);
-        return (int)c;
+    // one claim on the counter.  The claim that returns total - 1 is the last
+    // one of the launch (each workgroup claims until it passes the last item, so
+    // claims 0 .. total - 1 are made), and whoever holds it stores 0 back
+    // (settle) for the next launch that uses this workspace.  Inside the item
+    // loop the claim's value is first looked at when the item ends: a look at
+    // once would make the wave wait for every load it has in flight.
+    auto claim = [&]() { return (int)atomicAdd(a.ticket, 1u); };
+    auto settle = [&](int c) {
+        if ((unsigned)c == (unsigned)total - 1u) atomicExch(a.ticket, 0u);
     };
     if (dyn) {
-        if (tid == 0) s_next[1] = blockIdx.x < total ? (int)gridDim.x + claim() : total;
+        if (tid == 0 && (int)blockIdx.x < total) {
+            const int c = claim();
+            settle(c);
+            s_next[1] = (int)gridDim.x + c;
+        } else if (tid == 0) {
+            s_next[1] = total;
+        }
         __syncthreads();
     }
 
@@ -634,6 +686,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
         const bool have_next = following < total;
         const Item NI = item_info(have_next ? following : item);
         const int s = I.s, g = I.g, h0 = I.h0, nh = I.nh, k = I.kr, nparts = I.nparts;
+        finish_q();
 
         // running softmax state of this wave's keys: m per head (uniform), the
         // same m per logit slot of this lane, l per logit slot, acc per column
@@ -760,7 +813,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
                             for (int k2 = 0; k2 < 4; ++k2) v[4 * i + k2] = dk[nq][i][k2];
                         tbfly_blocks<8, 16>(v, lane);
                         const bool ok = key_ok && 4 * nq + hr < GT;
-                        x[nq] = ok ? (v[0] + qkb[nq]) * t.sc[0] * a.scale_log2 : -INFINITY;
+                        x[nq] = ok ? (v[0] + qkb[nq]) * (float)t.sc[0] * a.scale_log2 : -INFINITY;
                         over |= x[nq] > m_lane[nq] + kRescale;
                     }
                     softmax_update(x, over, r);
@@ -813,7 +866,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
                             for (int k2 = 0; k2 < 4; ++k2) v[4 * i + k2] = dk[nq][i][k2];
                         tbfly_blocks<16, 32>(v, lane);
                         const bool ok = key_ok && 4 * nq + hr < GT;
-                        const float sc = is_i8(KV) ? t.sc[0] : 1.0f;
+                        const float sc = is_i8(KV) ? (float)t.sc[0] : 1.0f;
                         x[nq] = ok ? (v[0] + qkb[nq]) * sc * a.scale_log2 : -INFINITY;
                         over |= x[nq] > m_lane[nq] + kRescale;
                     }
@@ -854,7 +907,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
                             for (int w = 0; w < 4; ++w)
                                 d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, cw[w]),
                                                                     __builtin_bit_cast(bf16x2_t, qb[j][w]), d, false);
-                            part[i * GT + j] = (d - 128.0f * qsum[j]) * t.sc[i];
+                            part[i * GT + j] = (d - 128.0f * qsum[j]) * (float)t.sc[i];
                         }
                     } else {
                         float x[C::EPL];
@@ -864,7 +917,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
                             float d = 0.0f;
 #pragma unroll
                             for (int e = 0; e < C::EPL; ++e) d = fmaf(qf[j][e], x[e], d);
-                            if constexpr (KV == KV_I8) d = (d - 128.0f * qsum[j]) * t.sc[i];
+                            if constexpr (KV == KV_I8) d = (d - 128.0f * qsum[j]) * (float)t.sc[i];
                             part[i * GT + j] = d;
                         }
                     }
@@ -943,7 +996,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
                             const bool row_ok = full || (blk_ok && tok >= c0 && tok < c1);
                             const float pj = lp[r * C::GTP + (j < GT ? j : 0)];
                             if constexpr (is_i8(KV)) {
-                                w[i] = (row_ok && j < GT) ? pj * t.sc[i] : 0.0f;
+                                w[i] = (row_ok && j < GT) ? pj * (float)t.sc[i] : 0.0f;
                                 psl[nq] += w[i];
                             } else {
                                 w[i] = (row_ok && j < GT) ? pj : 0.0f;
@@ -1028,7 +1081,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
                     if constexpr (is_i8(KV)) {
 #pragma unroll
                         for (int j = 0; j < GT; ++j) {
-                            p[j] = row_ok ? p[j] * t.sc[i] : 0.0f;
+                            p[j] = row_ok ? p[j] * (float)t.sc[i] : 0.0f;
                             psum[j] += p[j];
                         }
                     }
@@ -1058,7 +1111,16 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
             // followed by a V load and wait for every load at the next K step.
             if (nbw > 0) k_step(tk, it);
             if (!more && have_next) load_q(NI);
-            const int64_t t_n = (int64_t)__builtin_amdgcn_readlane(valid_id(id_n) ? id_n : 0, 0) * a.num_kv_heads + g_n;
+            // the wave's first block of that batch, read again through the scalar
+            // cache: a use of id_n here would wait for every load in flight (the
+            // loads of this batch may number zero, so the compiler cannot count
+            // them), the V tile of this step included
+            int id0 = -1;
+            {
+                const int col0 = jc0 / kBlk + wave - J.off;
+                if (nbw_n > 0 && col0 >= 0 && col0 < a.max_blocks) id0 = s_table[(int64_t)J.s * a.max_blocks + col0];
+            }
+            const int64_t t_n = (int64_t)(valid_id(id0) ? id0 : 0) * a.num_kv_heads + g_n;
             load_k(tk, t_n);
             __builtin_amdgcn_sched_barrier(0);
             if (nbw > 0) v_step(tv, it);
@@ -1127,7 +1189,10 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
             }
             // the item after the following one; every wave read this slot
             // before the previous item's barrier
-            if (dyn && wave == 0) s_next[parity] = following < total ? (int)gridDim.x + claimed : total;
+            if (dyn && wave == 0) {
+                if (following < total) settle(claimed);
+                s_next[parity] = following < total ? (int)gridDim.x + claimed : total;
+            }
         }
         // One barrier per item: the buffers alternate, so a wave that runs ahead
         // writes the other buffer, and it can only come back to this one after
