@@ -1165,21 +1165,43 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
 #pragma unroll
                 for (int e = 0; e < C::EPL; ++e) acc[j][e] -= 128.0f * psum[j];
         }
-#pragma unroll
-        for (int j = 0; j < GT; ++j)
-#pragma unroll
-            for (int e = 0; e < C::EPL; ++e) {
-                float v = acc[j][e];
-#pragma unroll
-                for (int off = C::LPR; off < kWave; off <<= 1) v += __shfl_xor(v, off, kWave);
-                acc[j][e] = v;
-            }
         float* cb = s_comb[parity][wave];
-        if (lane < C::LPR) {
+        if constexpr (C::LPR == 16 && (GT * C::EPL) % 4 == 0) {
+            // the lanes of a column are lane bits 4 and 5 apart: a transposed
+            // reduction over those bits by lane swaps leaves each lane a quarter
+            // of the GT x EPL sums, the ones of rows base .. base + N/4 - 1
+            constexpr int N = GT * C::EPL, H = N / 2, Q = N / 4;
+            float v[N];
 #pragma unroll
             for (int j = 0; j < GT; ++j)
 #pragma unroll
-                for (int e = 0; e < C::EPL; ++e) cb[j * D + col + e] = acc[j][e];
+                for (int e = 0; e < C::EPL; ++e) v[j * C::EPL + e] = acc[j][e];
+#pragma unroll
+            for (int q = 0; q < H; ++q) v[q] = swap_add<32>(v[q], v[H + q]);
+#pragma unroll
+            for (int q = 0; q < Q; ++q) v[q] = swap_add<16>(v[q], v[Q + q]);
+            const int base = ((lane >> 5) & 1) * H + ((lane >> 4) & 1) * Q;
+#pragma unroll
+            for (int q = 0; q < Q; ++q) {
+                const int idx = base + q;
+                cb[(idx / C::EPL) * D + col + idx % C::EPL] = v[q];
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < GT; ++j)
+#pragma unroll
+                for (int e = 0; e < C::EPL; ++e) {
+                    float v = acc[j][e];
+#pragma unroll
+                    for (int off = C::LPR; off < kWave; off <<= 1) v += __shfl_xor(v, off, kWave);
+                    acc[j][e] = v;
+                }
+            if (lane < C::LPR) {
+#pragma unroll
+                for (int j = 0; j < GT; ++j)
+#pragma unroll
+                    for (int e = 0; e < C::EPL; ++e) cb[j * D + col + e] = acc[j][e];
+            }
         }
         if (lane == 0) {
 #pragma unroll
