@@ -1294,7 +1294,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
 // depend on the weights, so they are issued together with the loads of the
 // maxima: a row of up to kMergeBatch partitions (most rows) waits for memory
 // once.
-constexpr int kMergeBatch = 8;
+constexpr int kMergeBatch = 16;
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecodeArgs a) {
