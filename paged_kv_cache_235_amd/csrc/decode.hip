@@ -1221,25 +1221,31 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
         // every wave has passed the next item's barrier, i.e. finished reading.
         // The barrier waits for LDS only; the next item's loads stay in flight.
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        // The waves' partial rows, rescaled to the common maximum and summed:
-        // every round's LDS reads and arithmetic first (rows past GT read row
-        // GT - 1, in bounds, and are not stored), so the rounds overlap, then
-        // the stores.
-        constexpr int R = (GT * D + kThreads - 1) / kThreads;
-        float ov[R], lv[R];
+        // The waves' partial rows, rescaled to the common maximum and summed,
+        // four adjacent columns per thread (one 16-byte LDS read per wave and
+        // one 16-byte store): every round's reads and arithmetic first (chunks
+        // past GT rows read row GT - 1, in bounds, and are not stored), so the
+        // rounds overlap, then the stores.
+        constexpr int NCH = GT * D / 4;
+        constexpr int R = (NCH + kThreads - 1) / kThreads;
+        f32x4_t ov[R];
+        float lv[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const int idx = tid + r * kThreads;
-            const int j = min(idx / D, GT - 1), d = idx % D;
+            const int c = tid + r * kThreads;
+            const int j = min(c / (D / 4), GT - 1), d0 = (c % (D / 4)) * 4;
             float M = -INFINITY;
 #pragma unroll
             for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_ml[parity][w][0][j]);
-            float o = 0.0f, l = 0.0f;
+            f32x4_t o = {0.0f, 0.0f, 0.0f, 0.0f};
+            float l = 0.0f;
 #pragma unroll
             for (int w = 0; w < kWaves; ++w) {
                 const float mw = s_ml[parity][w][0][j];
                 const float f = (mw == -INFINITY) ? 0.0f : fast_exp2(mw - M);
-                o = fmaf(f, s_comb[parity][w][j * D + d], o);
+                const f32x4_t x = *reinterpret_cast<const f32x4_t*>(&s_comb[parity][w][j * D + d0]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = fmaf(f, x[e], o[e]);
                 l = fmaf(f, s_ml[parity][w][1][j], l);
             }
             ov[r] = o;
@@ -1247,20 +1253,23 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
         }
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const int idx = tid + r * kThreads;
-            const int j = idx / D, d = idx % D;
-            if (idx >= GT * D || j >= nh) continue;
+            const int c = tid + r * kThreads;
+            const int j = c / (D / 4), d0 = (c % (D / 4)) * 4;
+            if (c >= NCH || j >= nh) continue;
             const int h = h0 + j;
             if (nparts == 1) {
-                const float q = lv[r] > 0.0f ? ov[r] / lv[r] : 0.0f;
-                const int64_t oi = ((int64_t)s * a.num_q_heads + h) * D + d;
-                if (a.out_bf16) static_cast<uint16_t*>(a.out)[oi] = f32_to_bf16(q);
-                else static_cast<float*>(a.out)[oi] = q;
+                const int64_t oi = ((int64_t)s * a.num_q_heads + h) * D + d0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float q = lv[r] > 0.0f ? ov[r][e] / lv[r] : 0.0f;
+                    if (a.out_bf16) static_cast<uint16_t*>(a.out)[oi + e] = f32_to_bf16(q);
+                    else static_cast<float*>(a.out)[oi + e] = q;
+                }
             } else {
                 // streaming stores: written once, read once by the merge; through
                 // the cache they measured ~2% of the call slower on the large batch
                 const int64_t pi = ((int64_t)s * a.num_q_heads + h) * a.max_parts + k;
-                __builtin_nontemporal_store(ov[r], &a.part_o[pi * D + d]);
+                __builtin_nontemporal_store(ov[r], reinterpret_cast<f32x4_t*>(&a.part_o[pi * D + d0]));
             }
         }
         // the item's (m, l) pairs: adjacent lanes of wave 0 write the run of
