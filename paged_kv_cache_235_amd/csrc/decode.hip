@@ -14,8 +14,8 @@
 //    flight stay neighbours).  No host knowledge of the lengths is needed.  A
 //    batch whose every possible item has a workgroup needs no counter.  The
 //    counter clears itself: every workgroup stops at its first claim past the
-//    last item, so exactly `total` claims are made and the one that returns
-//    total - 1 is the last access of the launch; it stores 0 back.
+//    last item, so exactly `total` claims are made, and the workgroup whose
+//    claim returns total - 1 (the last claim of the launch) stores 0 back.
 //  * Inside an item the 4 waves take the blocks round-robin.  Each wave streams
 //    its blocks' K and V tiles -- whole (block, KV head) runs, read with
 //    coalesced 16-byte loads -- as one sequence K0 V0 K1 V1 ..., each tile
@@ -27,13 +27,19 @@
 //    (with a rescale of what was accumulated) when a logit passes it by more
 //    than 2^8, which after the first tile is rare.  The probabilities go
 //    through LDS to the V step, which accumulates p * v (INT8 pools at
-//    head_dim 128: on the matrix cores, see the V step).  At the end of the
-//    item the 4 waves' (m, l, acc) are combined through LDS.
+//    head_dim 128, and bf16 pools with more than 4 heads per item: Q.K^T and
+//    P.V on the matrix cores, see the steps).  At the end of the item the 4
+//    waves' (m, l, acc) are combined through LDS.
+//  * Nothing in the stream waits for more than the tile it is about to use:
+//    values derived from a load (scales, query sums, the work counter's claim)
+//    are formed where they are used, and the ids and lengths an item needs
+//    before its first load are read through the scalar cache.
 //  * Keys outside the sequence, its window or a valid block are removed by
 //    selection (logit -inf, V row zeroed), never by multiplying by zero, so
 //    poisoned (NaN) tail slots cannot leak.
 //  * With more than one partition per sequence the items write unnormalised
-//    partial results (m, l, o) and a second kernel merges them (log-sum-exp).
+//    partial results (m, l, o) with streaming stores and a second kernel
+//    merges them (log-sum-exp).
 #include <mutex>
 
 #include "pkv_internal.h"
@@ -57,7 +63,7 @@ struct DecodeArgs {
     void* out;
     float* part_ml;          // [num_seqs][max_parts][Hq][2]  running max (log2 units), sum
     float* part_o;           // [num_seqs][Hq][max_parts][D]  unnormalised outputs
-    unsigned* ticket;        // item counter (zero at launch, zero again at exit), or null: items by stride
+    unsigned* ticket;        // item counter (zero at launch, zero again when the launch ends), or null: items by stride
     const char* k_pool;
     const char* v_pool;
     const uint16_t* k_scale;
@@ -670,12 +676,17 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
     constexpr bool MV = (is_i8(KV) || (KV == KV_BF16 && GT > 4)) && D == 128;
     constexpr int NHQ = (GT + 3) / 4;            // groups of 4 heads
     const int hr = lane & 3;                     // this lane's head within a group
-    // INT8 pools with a bf16 query, head_dim 128: Q.K^T on the matrix cores too.
-    // The K tile comes in the keys-by-lane layout (load_tile_keys_by_lane), so
-    // in an MFMA block A = K (row r: key 4i + r over 4 columns), B = Q^T (column
-    // r: head 4 nq + r at the same columns), D = the 4 x 4 partial logits over
-    // the block's 8 columns; a transposed butterfly across the 16 blocks then
-    // leaves each lane one logit per head group: key lane >> 2, head 4 nq + hr.
+    // INT8 pools with a bf16 query and bf16 pools with more than 4 heads per
+    // item, head_dim 128: Q.K^T on the matrix cores too.  The K tile comes
+    // keys-by-lane, so that in an MFMA block A = K (row r: one of four keys
+    // over 4 columns), B = Q^T (column r: head 4 nq + r at the same columns),
+    // D = the 4 x 4 partial logits over the block's columns; a transposed
+    // butterfly across the blocks that hold the same keys then leaves each lane
+    // one logit per head group, of head 4 nq + hr.  bf16
+    // (load_tile_keys_by_lane): 4 loads of keys 4i .. 4i+3, 8 columns per
+    // lane, butterfly over 16 blocks, key lane >> 2.  INT8
+    // (load_tile_keys_wide): 2 loads of keys 8i .. 8i+7, 16 columns per lane,
+    // butterfly over 8 column chunks, key wide_key(lane).
     constexpr bool MK = (KV == KV_I8Q || (KV == KV_BF16 && GT > 4)) && D == 128;
     constexpr int NS = MK ? NHQ : NT;            // logit slots per lane
 
