@@ -38,7 +38,7 @@
 //    selection (logit -inf, V row zeroed), never by multiplying by zero, so
 //    poisoned (NaN) tail slots cannot leak.
 //  * With more than one partition per sequence the items write unnormalised
-//    partial results (m, l, o) with streaming stores and a second kernel
+//    partial results (m, l, o) with device-scope stores and a second kernel
 //    merges them (log-sum-exp).
 #include <mutex>
 
@@ -227,6 +227,22 @@ __device__ __forceinline__ void load_tile_keys_by_lane(Tile<KV, D, GT>& t, const
 // 0-1 are lane bits 2-3, key bit 2 is lane bit 5, key bit 3 is lane bit 4.
 __device__ __forceinline__ int wide_key(int lane) {
     return ((lane >> 2) & 3) | ((lane >> 3) & 4) | ((lane >> 1) & 8);
+}
+
+// Stores of the split-K partials, which the merge kernel (possibly on another
+// XCD) reads next: device-scope stores (SC1), written through to the level
+// the XCDs share.  Through the cache they measured ~4% of the call slower on
+// the large batch, as streaming stores ~1% (and the merge reading them 1.2 us
+// slower).  `base` is the start of the run written (n bytes); offsets stay
+// small, so the buffer's 32-bit range suffices.
+constexpr int kCpolDeviceScope = 16;   // SC1: device scope
+__device__ __forceinline__ void store_partial4(float* base, int n, int byte_off, f32x4_t v) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, n, 0x00020000);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, byte_off, 0, kCpolDeviceScope);
+}
+__device__ __forceinline__ void store_partial1(float* base, int n, int byte_off, float v) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, n, 0x00020000);
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, byte_off, 0, kCpolDeviceScope);
 }
 
 // An INT8 K tile (head_dim 128) for Q.K^T on 4x4x4 MFMAs with 16-byte loads:
@@ -1277,10 +1293,11 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
                     else static_cast<float*>(a.out)[oi + e] = q;
                 }
             } else {
-                // streaming stores: written once, read once by the merge; through
-                // the cache they measured ~2% of the call slower on the large batch
-                const int64_t pi = ((int64_t)s * a.num_q_heads + h) * a.max_parts + k;
-                __builtin_nontemporal_store(ov[r], reinterpret_cast<f32x4_t*>(&a.part_o[pi * D + d0]));
+                // rows of the item's heads are max_parts * D floats apart; the
+                // base (the first head's row) is the same for the whole wave
+                const int64_t p0 = ((int64_t)s * a.num_q_heads + h0) * a.max_parts + k;
+                const int hstride = a.max_parts * D;
+                store_partial4(&a.part_o[p0 * D], ((nh - 1) * hstride + D) * 4, (j * hstride + d0) * 4, ov[r]);
             }
         }
         // the item's (m, l) pairs: adjacent lanes of wave 0 write the run of
@@ -1297,8 +1314,8 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
                 const float mw = s_ml[parity][w][0][j];
                 l = fmaf((mw == -INFINITY) ? 0.0f : fast_exp2(mw - M), s_ml[parity][w][1][j], l);
             }
-            const int64_t mi = (((int64_t)s * a.max_parts + k) * a.num_q_heads + h0) * 2 + lane;
-            __builtin_nontemporal_store((lane & 1) ? l : M, &a.part_ml[mi]);
+            const int64_t mi = (((int64_t)s * a.max_parts + k) * a.num_q_heads + h0) * 2;
+            store_partial1(&a.part_ml[mi], 2 * nh * 4, lane * 4, (lane & 1) ? l : M);
         }
         parity ^= 1;
         I = NI;
