@@ -51,8 +51,11 @@ __global__ __launch_bounds__(256) void kv_write_copy_kernel(WriteArgs a, int esz
         const int64_t dst = vec_index(slot, h, a) * a.head_dim * esz + c * 16;
         const u32x4_t kv = *reinterpret_cast<const u32x4_t*>(a.k + src);
         const u32x4_t vv = *reinterpret_cast<const u32x4_t*>(a.v + src);
-        *reinterpret_cast<u32x4_t*>(a.k_pool + dst) = kv;
-        *reinterpret_cast<u32x4_t*>(a.v_pool + dst) = vv;
+        // streaming stores: the pool is read back much later, in pieces (65,536
+        // tokens: 112 -> 88 us against plain stores; streaming loads as well
+        // measured slower, 110 us)
+        __builtin_nontemporal_store(kv, reinterpret_cast<u32x4_t*>(a.k_pool + dst));
+        __builtin_nontemporal_store(vv, reinterpret_cast<u32x4_t*>(a.v_pool + dst));
     }
 }
 
@@ -118,7 +121,8 @@ __global__ __launch_bounds__(256) void kv_write_int8_kernel(WriteArgs a) {
             if (store) {
                 const int64_t vec = vec_index(slot, h, a);
                 char* pool = which ? a.v_pool : a.k_pool;
-                *reinterpret_cast<u32x2_t*>(pool + vec * D + part * 8) = codes;
+                // streaming stores, as in the copy (65,536 tokens: 122 -> 110 us)
+                __builtin_nontemporal_store(codes, reinterpret_cast<u32x2_t*>(pool + vec * D + part * 8));
                 if (part == 0) (which ? a.v_scale : a.k_scale)[vec] = __builtin_bit_cast(uint16_t, s16);
             }
         }
