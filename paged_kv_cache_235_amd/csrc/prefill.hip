@@ -544,8 +544,6 @@ __global__ __launch_bounds__(64 * W) void prefill_pipe_kernel(PrefillArgs a) {
     const float l_row = l_run + __shfl_xor(l_run, 32, kWave);
     if (!row_ok) return;
     const float inv = l_row > 0.0f ? 1.0f / l_row : 0.0f;
-    // streaming stores (INT8 window-4096 call 1.5-3.7% faster in A/B runs; the
-    // ring kernel's stores stay plain: streaming measured 2% slower there)
     const int64_t obase = ((int64_t)(q0 + tok) * a.num_q_heads + g * G + jh) * D;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
@@ -558,10 +556,10 @@ __global__ __launch_bounds__(64 * W) void prefill_pipe_kernel(PrefillArgs a) {
                 u32x2_t pk;
                 pk[0] = pack_bf16x2(r0_, r1_);
                 pk[1] = pack_bf16x2(r2_, r3_);
-                __builtin_nontemporal_store(pk, reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(a.out) + obase + d));
+                *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(a.out) + obase + d) = pk;
             } else {
                 f32x4_t fv = {r0_, r1_, r2_, r3_};
-                __builtin_nontemporal_store(fv, reinterpret_cast<f32x4_t*>(static_cast<float*>(a.out) + obase + d));
+                *reinterpret_cast<f32x4_t*>(static_cast<float*>(a.out) + obase + d) = fv;
             }
         }
 }
