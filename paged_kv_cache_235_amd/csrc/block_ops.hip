@@ -67,8 +67,9 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyArgs a) {
          c += (int64_t)gridDim.y * blockDim.x) {
         const u32x4_t kv = ks[c];
         const u32x4_t vv = vs[c];
-        kd[c] = kv;
-        vd[c] = vv;
+        // streaming stores of whole lines (256 Llama-shaped blocks: 5.25 -> 4.87 us)
+        __builtin_nontemporal_store(kv, kd + c);
+        __builtin_nontemporal_store(vv, vd + c);
     }
     if (a.scale_words > 0 && blockIdx.y == 0) {
         const uint32_t* kss = reinterpret_cast<const uint32_t*>(a.k_scale) + (int64_t)s * a.scale_words;
