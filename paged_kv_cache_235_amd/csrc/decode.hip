@@ -363,7 +363,9 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int s = tid * per + i;
-            cnt[i] = (i < per && s < B) ? num_parts(a, s) : 0;
+            // partitions before the last one (the last ones are items of their own
+            // at the end of the order)
+            cnt[i] = (i < per && s < B) ? num_parts(a, s) - 1 : 0;
             sum += cnt[i];
         }
         // inclusive prefix of the per-thread sums: inside each wave by shuffles,
@@ -394,7 +396,13 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
     }
 
     const int HC = a.num_kv_heads * a.head_chunks;
-    const int total = direct ? B * HC : s_prefix[B] * HC;
+    // Items in claim order: first every partition but each sequence's last
+    // (s_prefix counts them), then the last partition of every sequence, one
+    // per sequence -- usually the short ones, so the launch ends on short items
+    // (a last-claimed full partition leaves its workgroup's neighbours idle for
+    // up to an item's time).
+    const int nfull = direct ? 0 : s_prefix[B];
+    const int total = direct ? B * HC : (nfull + B) * HC;
     const int row_lane = lane / C::LPR;          // row of this lane inside each load
     const int col = (lane % C::LPR) * C::EPL;    // first column of this lane
 
@@ -424,14 +432,21 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeArgs a
             I.nh = min(GT, a.group - hchunk * GT);
             return I;
         } else {
-            int lo_s = 0, hi_s = B - 1;             // largest s with s_prefix[s] <= gp
-            while (lo_s < hi_s) {
-                const int mid = (lo_s + hi_s + 1) >> 1;
-                if (uni(s_prefix[mid]) <= gp) lo_s = mid; else hi_s = mid - 1;
+            if (gp < nfull) {
+                int lo_s = 0, hi_s = B - 1;             // largest s with s_prefix[s] <= gp
+                while (lo_s < hi_s) {
+                    const int mid = (lo_s + hi_s + 1) >> 1;
+                    if (uni(s_prefix[mid]) <= gp) lo_s = mid; else hi_s = mid - 1;
+                }
+                I.s = lo_s;
+                ps = uni(s_prefix[I.s]);
+            } else {
+                // the last partition of sequence gp - nfull: as if its index
+                // were counted after the sequence's others
+                I.s = gp - nfull;
+                ps = gp - (uni(s_prefix[I.s + 1]) - uni(s_prefix[I.s]));   // kr = the count before it
             }
-            I.s = lo_s;
-            ps = uni(s_prefix[I.s]);
-            I.nparts = uni(s_prefix[I.s + 1]) - ps;
+            I.nparts = uni(s_prefix[I.s + 1]) - uni(s_prefix[I.s]) + 1;
             L = uni(s_len[I.s]);
         }
         const int off = seq_off_uniform(a, I.s);
