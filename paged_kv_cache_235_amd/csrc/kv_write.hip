@@ -35,6 +35,13 @@ __device__ __forceinline__ int64_t vec_index(int64_t slot, int h, const WriteArg
     return (blk * a.num_kv_heads + h) * a.block_size + off;
 }
 
+// The same for 0 <= slot < 2^32.
+__device__ __forceinline__ int64_t vec_index32(uint32_t slot, int h, const WriteArgs& a) {
+    const uint32_t blk = slot / (uint32_t)a.block_size;
+    const uint32_t off = slot - blk * (uint32_t)a.block_size;
+    return ((int64_t)blk * a.num_kv_heads + h) * a.block_size + off;
+}
+
 __global__ __launch_bounds__(256) void kv_write_copy_kernel(WriteArgs a, int esz) {
     const int chunks = a.head_dim * esz / 16;            // 16-byte chunks per vector
     const int64_t per_token = (int64_t)a.num_kv_heads * chunks;
@@ -79,6 +86,44 @@ __device__ __forceinline__ u32x2_t quantise8(const float* x, float sf) {
     return out;
 }
 
+// The same codes for bf16 inputs, with one multiplication by the scale's
+// reciprocal in place of each division.  Why the result is the same: write
+// x = mx 2^a (|mx| < 2^8, a bf16 value) and sf = ms 2^b (0 < ms < 2^11, a
+// binary16 value).  For a half-integer h, x - h sf is a multiple of
+// 2^min(a, b-1), so either x / sf = h exactly or |x / sf - h| >=
+// min(2^(a-b) / ms, 1 / (2 ms)) >= 2^-12 (the first term is |x / sf| / |mx|,
+// and h is only in reach once |x / sf| >= 1/4).  The product x * rcp(sf),
+// with the reciprocal within 1 ulp and one rounding, is within 2^-22
+// relative, i.e. < 2^-14 absolute for |x / sf| <= 191 (the largest ratio a
+// binary16-rounded scale allows).  So when the product is at least 2^-13 from
+// every half-integer, x / sf and its fp32 rounding lie on the same side of
+// every half-integer as the product and all three round to the same integer.
+// A lane with a product closer than that (exact ties among them) takes the
+// IEEE divisions.  NaN, infinite and zero inputs give what the divisions give.
+__device__ __forceinline__ u32x2_t quantise8_bf16(const float* x, float sf) {
+    if (sf == 0.0f) return u32x2_t{0u, 0u};
+    const float r = __builtin_amdgcn_rcpf(sf);
+    float c[8];
+    bool near = false;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float q = x[e] * r;
+        c[e] = __builtin_rintf(q);
+        near |= fabsf(q - c[e]) > 0.5f - 0x1p-13f;
+    }
+    if (near) return quantise8(x, sf);
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int q = (int)fminf(fmaxf(c[e], -127.0f), 127.0f);
+        w[e >> 2] |= ((uint32_t)(q & 0xff)) << (8 * (e & 3));
+    }
+    u32x2_t out;
+    out[0] = w[0];
+    out[1] = w[1];
+    return out;
+}
+
 template <bool IN_BF16, int D>
 __global__ __launch_bounds__(256) void kv_write_int8_kernel(WriteArgs a) {
     constexpr int GL = D / 8;                        // lanes per vector
@@ -86,8 +131,12 @@ __global__ __launch_bounds__(256) void kv_write_int8_kernel(WriteArgs a) {
     const int64_t gid = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / GL;
     const int part = threadIdx.x % GL;
     // every lane of a group takes the same trip count, so the group reductions stay converged
+    // 32-bit divisions where the sizes allow (a uniform branch)
+    const bool narrow = vecs <= (int64_t)UINT32_MAX && a.num_slots <= (int64_t)UINT32_MAX;
     for (int64_t vi = gid; vi < vecs; vi += (int64_t)gridDim.x * blockDim.x / GL) {
-        const int64_t t = vi / a.num_kv_heads;
+        int64_t t;
+        if (narrow) t = (uint32_t)vi / (uint32_t)a.num_kv_heads;
+        else t = vi / a.num_kv_heads;
         const int h = (int)(vi - t * a.num_kv_heads);
         const int64_t slot = a.slots[t];
         const bool store = slot >= 0 && slot < a.num_slots;
@@ -117,9 +166,11 @@ __global__ __launch_bounds__(256) void kv_write_int8_kernel(WriteArgs a) {
             am = group_max<GL>(am);
             const _Float16 s16 = (_Float16)__fdiv_rn(am, 127.0f);   // RNE to binary16
             const float sf = (float)s16;
-            const u32x2_t codes = quantise8(x, sf);
+            u32x2_t codes;
+            if constexpr (IN_BF16) codes = quantise8_bf16(x, sf);
+            else codes = quantise8(x, sf);
             if (store) {
-                const int64_t vec = vec_index(slot, h, a);
+                const int64_t vec = narrow ? vec_index32((uint32_t)slot, h, a) : vec_index(slot, h, a);
                 char* pool = which ? a.v_pool : a.k_pool;
                 // streaming stores, as in the copy (65,536 tokens: 122 -> 110 us)
                 __builtin_nontemporal_store(codes, reinterpret_cast<u32x2_t*>(pool + vec * D + part * 8));
