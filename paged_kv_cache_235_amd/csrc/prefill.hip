@@ -297,9 +297,7 @@ __global__ __launch_bounds__(64 * W) void prefill_pipe_kernel(PrefillArgs a) {
                 }
             }
         } else if (v_task) {
-            uint32_t w[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) w[i] = vreg[i];
+            uint32_t* w = vreg;
             if (m != 15 || kt + kKeys > L) {    // edge tile (uniform branch): zero dead keys, they may hold NaN
                 const bool blk_live = (m >> (v_kg / 2)) & 1;
 #pragma unroll
@@ -352,6 +350,8 @@ __global__ __launch_bounds__(64 * W) void prefill_pipe_kernel(PrefillArgs a) {
     // the factor that turns an accumulated score into log2 units (INT8: the
     // per-key factor is already applied)
     const float sl2 = I8 ? 1.0f : a.scale_log2;
+    const int xaddr = (lane ^ 32) << 2;        // ds_bpermute address of lane ^ 32
+    float msub = 0.0f;                         // m_used, or 0 while it is -inf
     auto finish_tile = [&](f32x16_t* S, f32x16_t* S_nxt, int buf, int kt, int tmask) {
         if constexpr (I8) {
             // score of key j times scale_j * softmax scale * log2 e (before masking: a
@@ -389,13 +389,18 @@ __global__ __launch_bounds__(64 * W) void prefill_pipe_kernel(PrefillArgs a) {
         for (int T = 0; T < 2; ++T)
 #pragma unroll
             for (int v = 0; v < 16; ++v) mt_ = fmaxf(mt_, S[T][v]);
-        mt_ = fmaxf(mt_, __shfl_xor(mt_, 32, kWave));
-        const float m_tile = mt_ == -INFINITY ? -INFINITY : mt_ * sl2;
-        const bool grow = m_tile > m_used + kRescale || (m_used == -INFINITY && m_tile != -INFINITY);
+        mt_ = fmaxf(mt_, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(xaddr, __builtin_bit_cast(int, mt_))));
+        // with a positive scale, m_used + 8 stays -inf until the row's first visible
+        // key, so the comparison alone starts the running maximum, and 2^(m_used -
+        // m_new) is then 2^-inf = 0 (a zero scale keeps the explicit guards)
+        const float m_tile = (ZS && mt_ == -INFINITY) ? -INFINITY : mt_ * sl2;
+        const bool grow = ZS ? (m_tile > m_used + kRescale || (m_used == -INFINITY && m_tile != -INFINITY))
+                             : m_tile > m_used + kRescale;
         if (__builtin_amdgcn_ballot_w64(grow)) {
             const float m_new = grow ? m_tile : m_used;
-            const float alpha = (m_used == -INFINITY) ? 0.0f : fast_exp2(m_used - m_new);
+            const float alpha = (ZS && m_used == -INFINITY) ? 0.0f : fast_exp2(m_used - m_new);
             m_used = m_new;
+            msub = (m_used == -INFINITY) ? 0.0f : m_used;
             const float f = grow ? alpha : 1.0f;
             l_run *= f;
 #pragma unroll
@@ -403,7 +408,6 @@ __global__ __launch_bounds__(64 * W) void prefill_pipe_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) o[nt][v] *= f;
         }
-        const float msub = (m_used == -INFINITY) ? 0.0f : m_used;
         compute_s(S_nxt, buf ^ 1);
         // V^T row d = 32 nt + (lane & 31), key group 2 ks + h, at one base + constants
         const uint16_t* vt_base = &s_vt[buf][(lane & 31) * kVtStride + 8 * (h ^ ((lane >> 4) & 1))];
@@ -782,9 +786,7 @@ void prefill_ring_kernel(PrefillArgs a) {
 #pragma unroll
         for (int n = 0; n < NVP; ++n) {
             const int v_kg = wave + W * n;
-            uint32_t w[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) w[i] = vreg[n][i];
+            uint32_t* w = vreg[n];
             if (m != 15 || kt + kKeys > L) {    // edge tile (uniform branch): zero dead keys, they may hold NaN
                 const bool blk_live = (m >> (v_kg / 2)) & 1;
 #pragma unroll
@@ -832,6 +834,8 @@ void prefill_ring_kernel(PrefillArgs a) {
     // the next tile's S^T MFMAs (from K slot slot ^ 1) go out in the same basic
     // block as the exp2 work.  On the last tile that slot holds stale data: the
     // MFMAs read in-bounds LDS and the result is never used.
+    const int xaddr = (lane ^ 32) << 2;        // ds_bpermute address of lane ^ 32
+    float msub = 0.0f;                         // m_used, or 0 while it is -inf
     const float sl2 = a.scale_log2;
     auto finish_tile = [&](f32x16_t* S, f32x16_t* S_nxt, int slot, int kt, int tmask) {
         const bool full = tmask == 15 && kt + kKeys - 1 <= p_min && (a.window <= 0 || kt >= p_max - a.window + 1);
@@ -851,13 +855,18 @@ void prefill_ring_kernel(PrefillArgs a) {
         for (int T = 0; T < 2; ++T)
 #pragma unroll
             for (int v = 0; v < 16; ++v) mt_ = fmaxf(mt_, S[T][v]);
-        mt_ = fmaxf(mt_, __shfl_xor(mt_, 32, kWave));
-        const float m_tile = mt_ == -INFINITY ? -INFINITY : mt_ * sl2;
-        const bool grow = m_tile > m_used + kRescale || (m_used == -INFINITY && m_tile != -INFINITY);
+        mt_ = fmaxf(mt_, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(xaddr, __builtin_bit_cast(int, mt_))));
+        // with a positive scale, m_used + 8 stays -inf until the row's first visible
+        // key, so the comparison alone starts the running maximum, and 2^(m_used -
+        // m_new) is then 2^-inf = 0 (a zero scale keeps the explicit guards)
+        const float m_tile = (ZS && mt_ == -INFINITY) ? -INFINITY : mt_ * sl2;
+        const bool grow = ZS ? (m_tile > m_used + kRescale || (m_used == -INFINITY && m_tile != -INFINITY))
+                             : m_tile > m_used + kRescale;
         if (__builtin_amdgcn_ballot_w64(grow)) {
             const float m_new = grow ? m_tile : m_used;
-            const float alpha = (m_used == -INFINITY) ? 0.0f : fast_exp2(m_used - m_new);
+            const float alpha = (ZS && m_used == -INFINITY) ? 0.0f : fast_exp2(m_used - m_new);
             m_used = m_new;
+            msub = (m_used == -INFINITY) ? 0.0f : m_used;
             const float f = grow ? alpha : 1.0f;
             l_run *= f;
 #pragma unroll
@@ -865,7 +874,6 @@ void prefill_ring_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) o[nt][v] *= f;
         }
-        const float msub = (m_used == -INFINITY) ? 0.0f : m_used;
         compute_s(S_nxt, slot ^ 1);
         const uint16_t* vt_base = &s_vt[slot][(lane & 31) * kVtStride + 8 * (h ^ ((lane >> 4) & 1))];
         uint32_t pw[2][8];                       // P^T as fp16 pairs: [T][4u + word]
