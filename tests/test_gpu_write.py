@@ -124,3 +124,52 @@ def test_empty_write_is_a_no_op():
     pkv.kv_cache_write(e, e, torch.empty(0, dtype=torch.int32, device=dev), kp, vp)
     torch.cuda.synchronize()
     assert torch.isnan(kp).all()
+
+
+def test_int8_bf16_exact_ties_across_scales():
+    """bf16 inputs quantise by a reciprocal product and fall back to the IEEE
+    division only near half-integers ("MicroGen", Key Features: dynamic
+    per-vector INT8 KV; the codes must still be the division's).  Each vector
+    sets its scale with one element of 127 sf, so the scale is sf exactly for
+    sf = 2^k (k = -24..15) and lands on the subnormal binary16 grid for sf =
+    j 2^-24; half of it holds exact ties x = h sf (every such lane takes the
+    fallback, and rounds half to even) and half random bf16 values up to the
+    absmax (the product path).  Bit-exact against the oracle."""
+    d = 128
+    rng = np.random.default_rng(23)
+    mults = [1] * 40 + [1, 3, 5, 7, 11]                              # sf = mult * 2^e
+    scales = [2.0 ** e for e in range(-24, 16)] + [j * 2.0 ** -24 for j in (1, 3, 5, 7, 11)]
+    rows = []
+    for sf, j in zip(scales, mults):
+        for rep in range(2):
+            x = np.empty(d, np.float64)
+            x[0] = 127.0 * sf * (1 if rep == 0 else -1)
+            odd = 2 * rng.integers(0, 127, size=63) + 1             # h = odd / 2 <= 126.5 < 127
+            top = 255 // j - (1 - (255 // j) % 2)                   # largest odd with odd * j <= 255
+            odd = np.minimum(odd, top)                              # so that x = odd * j 2^(e-1) is bf16
+            x[1:64] = (odd / 2.0) * sf * rng.choice([-1.0, 1.0], size=63)
+            x[64:] = rng.uniform(-1.0, 1.0, size=64) * 127.0 * sf
+            rows.append(x)
+    xb = torch.from_numpy(np.stack(rows)).to(torch.float32).to(torch.bfloat16)   # [T][D]
+    T = xb.shape[0]
+    dev = device()
+    k = xb.view(T, 1, d).to(dev)
+    nb = (T + 15) // 16 + 1
+    slots = torch.randperm(nb * 16, generator=torch.Generator().manual_seed(5))[:T].to(torch.int32).to(dev)
+    kp = torch.full((nb, 1, 16, d), -128, dtype=torch.int8, device=dev)
+    vp = kp.clone()
+    ksc = torch.full((nb, 1, 16), float("nan"), dtype=torch.float16, device=dev)
+    vsc = ksc.clone()
+    pkv.kv_cache_write(k, k, slots, kp, vp, ksc, vsc)
+    torch.cuda.synchronize()
+    ref = oracle.Cache(nb, 16, 1, d, "i8")
+    xh = to_numpy(xb.view(T, 1, d))
+    ref.write(xh, xh, "bf16", slots.cpu().numpy())
+    assert np.array_equal(_bits(kp), ref.k)
+    assert np.array_equal(_bits(vp), ref.v)
+    assert np.array_equal(_bits(ksc), ref.k_scale)
+    # the ties are really ties: for the power-of-two scales, |x| / sf is a half-integer
+    xs = xb.to(torch.float32).numpy()
+    for i, sf in enumerate(scales):
+        q = np.abs(xs[2 * i, 1:64]) / np.float32(sf)
+        assert np.array_equal(q - np.floor(q), np.full(63, 0.5, np.float32))
