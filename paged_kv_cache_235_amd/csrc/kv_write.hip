@@ -130,9 +130,9 @@ __global__ __launch_bounds__(256) void kv_write_int8_kernel(WriteArgs a) {
     const int64_t vecs = (int64_t)a.num_tokens * a.num_kv_heads;
     const int64_t gid = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / GL;
     const int part = threadIdx.x % GL;
-    // every lane of a group takes the same trip count, so the group reductions stay converged
     // 32-bit divisions where the sizes allow (a uniform branch)
     const bool narrow = vecs <= (int64_t)UINT32_MAX && a.num_slots <= (int64_t)UINT32_MAX;
+    // every lane of a group takes the same trip count, so the group reductions stay converged
     for (int64_t vi = gid; vi < vecs; vi += (int64_t)gridDim.x * blockDim.x / GL) {
         int64_t t;
         if (narrow) t = (uint32_t)vi / (uint32_t)a.num_kv_heads;

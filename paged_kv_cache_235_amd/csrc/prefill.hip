@@ -830,12 +830,12 @@ void prefill_ring_kernel(PrefillArgs a) {
         }
     };
 
+    const int xaddr = (lane ^ 32) << 2;        // ds_bpermute address of lane ^ 32
+    float msub = 0.0f;                         // m_used, or 0 while it is -inf
     // masks, online softmax and O^T += V^T P^T for tile t (scores in S, V in slot);
     // the next tile's S^T MFMAs (from K slot slot ^ 1) go out in the same basic
     // block as the exp2 work.  On the last tile that slot holds stale data: the
     // MFMAs read in-bounds LDS and the result is never used.
-    const int xaddr = (lane ^ 32) << 2;        // ds_bpermute address of lane ^ 32
-    float msub = 0.0f;                         // m_used, or 0 while it is -inf
     const float sl2 = a.scale_log2;
     auto finish_tile = [&](f32x16_t* S, f32x16_t* S_nxt, int slot, int kt, int tmask) {
         const bool full = tmask == 15 && kt + kKeys - 1 <= p_min && (a.window <= 0 || kt >= p_max - a.window + 1);
