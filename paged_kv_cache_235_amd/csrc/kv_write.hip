@@ -115,7 +115,8 @@ __device__ __forceinline__ u32x2_t quantise8_bf16(const float* x, float sf) {
     uint32_t w[2] = {0u, 0u};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        const int q = (int)fminf(fmaxf(c[e], -127.0f), 127.0f);
+        // clamp by one median (c comes from rint, so it is never a signalling NaN)
+        const int q = (int)__builtin_amdgcn_fmed3f(c[e], -127.0f, 127.0f);
         w[e >> 2] |= ((uint32_t)(q & 0xff)) << (8 * (e & 3));
     }
     u32x2_t out;
@@ -141,11 +142,18 @@ __global__ __launch_bounds__(256) void kv_write_int8_kernel(WriteArgs a) {
         const int64_t slot = a.slots[t];
         const bool store = slot >= 0 && slot < a.num_slots;
         const int64_t src = t * a.token_stride_bytes + (int64_t)h * D * (IN_BF16 ? 2 : 4);
+        // bf16: both vectors' loads in flight before either is quantised
+        u32x4_t wkv[2];
+        if constexpr (IN_BF16) {
+            wkv[0] = *reinterpret_cast<const u32x4_t*>(a.k + src + part * 16);
+            wkv[1] = *reinterpret_cast<const u32x4_t*>(a.v + src + part * 16);
+        }
+#pragma unroll
         for (int which = 0; which < 2; ++which) {
             const char* in = which ? a.v : a.k;
             float x[8];
             if constexpr (IN_BF16) {
-                const u32x4_t w = *reinterpret_cast<const u32x4_t*>(in + src + part * 16);
+                const u32x4_t w = wkv[which];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     x[2 * e] = bf16lo(w[e]);
