@@ -125,6 +125,20 @@ __device__ __forceinline__ u32x2_t quantise8_bf16(const float* x, float sf) {
     return out;
 }
 
+// Max over an aligned group of W <= 16 lanes of values that are >= +0 and never
+// NaN: their bit patterns order like the values, so an integer max does it
+// without the NaN canonicalisation a float max needs.
+template <int W>
+__device__ __forceinline__ float group_max_nonneg(float x) {
+    static_assert(W <= 16, "DPP exchanges within a row");
+    uint32_t u = __builtin_bit_cast(uint32_t, x);
+    if constexpr (W >= 16) u = max(u, __builtin_bit_cast(uint32_t, xchg<8>(__builtin_bit_cast(float, u))));
+    if constexpr (W >= 8) u = max(u, __builtin_bit_cast(uint32_t, xchg<4>(__builtin_bit_cast(float, u))));
+    if constexpr (W >= 4) u = max(u, __builtin_bit_cast(uint32_t, xchg<2>(__builtin_bit_cast(float, u))));
+    if constexpr (W >= 2) u = max(u, __builtin_bit_cast(uint32_t, xchg<1>(__builtin_bit_cast(float, u))));
+    return __builtin_bit_cast(float, u);
+}
+
 template <bool IN_BF16, int D>
 __global__ __launch_bounds__(256) void kv_write_int8_kernel(WriteArgs a) {
     constexpr int GL = D / 8;                        // lanes per vector
@@ -171,8 +185,11 @@ __global__ __launch_bounds__(256) void kv_write_int8_kernel(WriteArgs a) {
             float am = 0.0f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(x[e]));
-            am = group_max<GL>(am);
-            const _Float16 s16 = (_Float16)__fdiv_rn(am, 127.0f);   // RNE to binary16
+            am = group_max_nonneg<GL>(am);             // am >= +0, never NaN (fmaxf skips NaN)
+            // binary16(fp32(am / 127)), RNE.  For bf16 inputs am is a bf16 value, and for
+            // every one of those a multiplication by fp32(1/127) rounds to the same
+            // binary16 value as the IEEE quotient (checked over all of them on the host)
+            const _Float16 s16 = IN_BF16 ? (_Float16)(am * 0x1.020408p-7f) : (_Float16)__fdiv_rn(am, 127.0f);
             const float sf = (float)s16;
             u32x2_t codes;
             if constexpr (IN_BF16) codes = quantise8_bf16(x, sf);

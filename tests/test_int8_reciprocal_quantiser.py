@@ -15,6 +15,10 @@ their whole domain with numpy's IEEE binary32 arithmetic:
   neighbours), a product at least 2^-13 from every half-integer rounds to the
   integer the IEEE quotient rounds to.
 
+and, for the scale itself, that binary16(fp32(amax * fp32(1/127))) equals
+binary16(fp32(amax / 127)) for every bf16 amax (the kernel's scale of bf16
+inputs).
+
 Below x / sf = 1/8 both give 0 (the product is below 1/8 + 2^-20), and negative
 x mirror positive x (the product, the quotient and round-half-even are all odd
 functions).  This checks the kernel's arithmetic, not the oracle, and calls
@@ -89,3 +93,19 @@ def test_exact_ties_take_the_division():
         for r in (np.nextafter(r0, np.float32(0.0)), r0, np.nextafter(r0, np.float32(np.inf))):
             q = xv * r
             assert (np.abs(q - np.rint(q)) > THRESH).all(), h
+
+
+def test_scale_by_the_reciprocal_of_127():
+    # the write kernel takes the scale of bf16 inputs as binary16(fp32(amax * c)),
+    # c = fp32(1/127), in place of binary16(fp32(amax / 127)): amax is then a bf16
+    # value, and over every one of them (zero and infinity included) the two agree
+    bits = np.arange(0x0000, 0x7F81, dtype=np.uint32)             # +0 .. +inf
+    amax = (bits << 16).view(np.float32)
+    c = np.float32(float.fromhex("0x1.020408p-7"))
+    assert c == np.float32(1.0) / np.float32(127.0)
+    with np.errstate(over="ignore"):
+        by_division = (amax / np.float32(127.0)).astype(np.float16)
+        by_product = (amax * c).astype(np.float16)
+    assert np.array_equal(by_division.view(np.uint16), by_product.view(np.uint16))
+    # the fp32 values themselves differ often: only the binary16 rounding agrees
+    assert np.count_nonzero((amax / np.float32(127.0)) != (amax * c)) > 100
