@@ -767,15 +767,16 @@ def measured_peaks(torch):
     """What this GPU reaches, beside the published peaks the roofline fractions
     are quoted against.  The measurement kernels of include/pkv_probe.h: a
     streaming read of 4 GiB (far past the 256 MiB last-level cache; every
-    16-byte chunk read once, four loads in flight per thread) and bf16 MFMA
+    16-byte chunk read once, four loads in flight per thread, in grid-stride
+    order and in a contiguous span per workgroup) and bf16 MFMA
     chains with no memory traffic; best over a few grid sizes.  torch's copy
     and GEMM are given as library reference points.  Each rate is the mean over
     back-to-back launches between two events, after untimed launches."""
     import ctypes
     from paged_kv_cache_235_amd import _build
     plib = ctypes.CDLL(_build.PROBE_LIB_PATH)
-    plib.pkv_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32,
-                                           ctypes.c_void_p]
+    for f in (plib.pkv_probe_stream_read, plib.pkv_probe_stream_read_spans):
+        f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
     plib.pkv_probe_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_uint32,
                                          ctypes.c_void_p]
     dev = torch.device("cuda", 0)
@@ -799,12 +800,13 @@ def measured_peaks(torch):
     nbytes = 4 << 30
     buf = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
     threads = 256
-    read = {}
+    read, spans = {}, {}
     for grid in (2048, 4096, 8192, 16384, 32768):
         sink = torch.empty(grid * threads, dtype=torch.int32, device=dev)
-        t = seconds(lambda: call(plib.pkv_probe_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes,
-                                                            ctypes.c_void_p(sink.data_ptr()), grid, stream)), 10)
-        read[grid] = nbytes / t / 1e9
+        for fn, res in ((plib.pkv_probe_stream_read, read), (plib.pkv_probe_stream_read_spans, spans)):
+            t = seconds(lambda: call(fn(ctypes.c_void_p(buf.data_ptr()), nbytes,
+                                        ctypes.c_void_p(sink.data_ptr()), grid, stream)), 10)
+            res[grid] = nbytes / t / 1e9
     out = torch.empty_like(buf)
     t_copy = seconds(lambda: out.copy_(buf), 10)
     del buf, out
@@ -823,15 +825,17 @@ def measured_peaks(torch):
     t_mm = seconds(lambda: torch.matmul(a_, b_, out=c_), 20)
     del a_, b_, c_
     torch.cuda.empty_cache()
-    return {"hbm_read_GBps": round(max(read.values()), 1),
+    return {"hbm_read_GBps": round(max(max(read.values()), max(spans.values())), 1),
             "hbm_read_GBps_by_grid": {str(k): round(v, 1) for k, v in read.items()},
+            "hbm_read_spans_GBps_by_grid": {str(k): round(v, 1) for k, v in spans.items()},
             "bf16_mfma_TFLOPs": round(max(mfma.values()), 1),
             "bf16_mfma_TFLOPs_by_grid": {str(k): round(v, 1) for k, v in mfma.items()},
             "torch_copy_GBps": round(2 * nbytes / t_copy / 1e9, 1),
             "torch_bf16_gemm_8192_TFLOPs": round(2 * m ** 3 / t_mm / 1e12, 1),
-            "how": "pkv_probe_stream_read over 4 GiB and pkv_probe_mfma_bf16 (10000 rounds of 4 MFMA chains "
-                   "per wave), best grid; torch copy_ of 4 GiB (read + write) and torch.matmul of two 8192^2 "
-                   "bf16 matrices for reference"}
+            "how": "pkv_probe_stream_read (grid-stride order) and pkv_probe_stream_read_spans (a contiguous "
+                   "span per workgroup) over 4 GiB, the best of both orders and all grids; pkv_probe_mfma_bf16 "
+                   "(10000 rounds of 4 MFMA chains per wave), best grid; torch copy_ of 4 GiB (read + write) and "
+                   "torch.matmul of two 8192^2 bf16 matrices for reference"}
 
 
 def main():

@@ -5,7 +5,7 @@
  * (HBM 8 TB/s, dense bf16 matrix throughput 2.5 PFLOP/s).  They are not part of
  * the paged-attention path and share no code with it.
  *
- * Both calls launch on `stream` (NULL: the default stream), return at once, and
+ * Every call launches on `stream` (NULL: the default stream), returns at once, and
  * give 0 on success, 1 for a bad argument, 2 for a HIP launch error.
  */
 #ifndef PKV_PROBE_H
@@ -27,6 +27,13 @@ extern "C" {
  * grid-stride loop.  Each thread writes the XOR of what it read to
  * sink[global thread id], so sink must hold grid * PKV_PROBE_THREADS uint32_t. */
 int pkv_probe_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int32_t grid, hipStream_t stream);
+
+/* The same read with another order: workgroup w reads the contiguous span of
+ * chunks [w * span, (w + 1) * span), span = ceil(chunks / grid), in order, four
+ * loads in flight per thread; each chunk still exactly once.  Same arguments,
+ * buffer rules and sink. */
+int pkv_probe_stream_read_spans(const void* buf, int64_t bytes, uint32_t* sink, int32_t grid,
+                                hipStream_t stream);
 
 /* Matrix-core throughput: each wave runs `iters` rounds of four independent
  * chains of v_mfma_f32_32x32x16_bf16 on register operands (no memory traffic

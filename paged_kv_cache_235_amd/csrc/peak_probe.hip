@@ -32,6 +32,24 @@ __global__ __launch_bounds__(PKV_PROBE_THREADS) void stream_read_kernel(const u3
     sink[t] = acc.x ^ acc.y ^ acc.z ^ acc.w;
 }
 
+// workgroup w reads chunks [w span, min((w + 1) span, chunks)) once, in order
+__global__ __launch_bounds__(PKV_PROBE_THREADS) void stream_read_spans_kernel(const u32x4* buf, int64_t chunks,
+                                                                            int64_t span, uint32_t* sink) {
+    constexpr int T = PKV_PROBE_THREADS;
+    const int64_t start = (int64_t)blockIdx.x * span;
+    const int64_t end = start + span < chunks ? start + span : chunks;
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    int64_t i = start + threadIdx.x;
+    for (; i + 3 * T < end; i += 4 * T) {
+        const u32x4 a = __builtin_nontemporal_load(buf + i);
+        const u32x4 b = __builtin_nontemporal_load(buf + i + T);
+        const u32x4 c = __builtin_nontemporal_load(buf + i + 2 * T);
+        const u32x4 d = __builtin_nontemporal_load(buf + i + 3 * T);
+        acc ^= a ^ b ^ c ^ d;
+    }
+    for (; i < end; i += T) acc ^= __builtin_nontemporal_load(buf + i);
+    sink[(int64_t)blockIdx.x * T + threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
+}
 __global__ __launch_bounds__(PKV_PROBE_THREADS) void mfma_bf16_kernel(float* sink, int32_t iters, uint32_t seed) {
     const int t = blockIdx.x * PKV_PROBE_THREADS + threadIdx.x;
     // operands from the thread id and a run-time seed, small enough that the
@@ -67,6 +85,17 @@ extern "C" int pkv_probe_stream_read(const void* buf, int64_t bytes, uint32_t* s
     return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 
+extern "C" int pkv_probe_stream_read_spans(const void* buf, int64_t bytes, uint32_t* sink, int32_t grid,
+                                           hipStream_t stream) {
+    if (!buf || !sink || bytes <= 0 || bytes % 16 != 0 || grid <= 0 ||
+        reinterpret_cast<uintptr_t>(buf) % 16 != 0)
+        return 1;
+    const int64_t chunks = bytes / 16;
+    const int64_t span = (chunks + grid - 1) / grid;
+    stream_read_spans_kernel<<<dim3(grid), dim3(PKV_PROBE_THREADS), 0, stream>>>(static_cast<const u32x4*>(buf),
+                                                                                chunks, span, sink);
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
 extern "C" int pkv_probe_mfma_bf16(float* sink, int32_t iters, int32_t grid, uint32_t seed, hipStream_t stream) {
     if (!sink || iters < 0 || grid <= 0) return 1;
     mfma_bf16_kernel<<<dim3(grid), dim3(PKV_PROBE_THREADS), 0, stream>>>(sink, iters, seed);

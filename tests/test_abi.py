@@ -201,16 +201,16 @@ def test_probe_library_exports_its_header_and_rejects_bad_arguments():
         _build.build()
     plib = ctypes.CDLL(_build.PROBE_LIB_PATH)
     names = declared_functions(os.path.join(ROOT, "include", "pkv_probe.h"))
-    assert names == ["pkv_probe_mfma_bf16", "pkv_probe_stream_read"]
+    assert names == ["pkv_probe_mfma_bf16", "pkv_probe_stream_read", "pkv_probe_stream_read_spans"]
     for n in names:
         assert hasattr(plib, n), n
-    sr = plib.pkv_probe_stream_read
-    sr.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
-    assert sr(FAKE, 15, FAKE, 1, None) == 1          # not whole 16-byte chunks
-    assert sr(FAKE, 0, FAKE, 1, None) == 1
-    assert sr(FAKE, 16, FAKE, 0, None) == 1          # empty grid
-    assert sr(None, 16, FAKE, 1, None) == 1
-    assert sr(ctypes.c_void_p(0x1008), 16, FAKE, 1, None) == 1   # not 16-byte aligned
+    for sr in (plib.pkv_probe_stream_read, plib.pkv_probe_stream_read_spans):
+        sr.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+        assert sr(FAKE, 15, FAKE, 1, None) == 1          # not whole 16-byte chunks
+        assert sr(FAKE, 0, FAKE, 1, None) == 1
+        assert sr(FAKE, 16, FAKE, 0, None) == 1          # empty grid
+        assert sr(None, 16, FAKE, 1, None) == 1
+        assert sr(ctypes.c_void_p(0x1008), 16, FAKE, 1, None) == 1   # not 16-byte aligned
     mm = plib.pkv_probe_mfma_bf16
     mm.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_uint32, ctypes.c_void_p]
     assert mm(FAKE, -1, 1, 0, None) == 1
